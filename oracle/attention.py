@@ -1,0 +1,117 @@
+"""Plain float64 reference for the exact attention forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import or call this
+module; only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+
+What it computes is the textbook definition the FlashAttention pages start
+from (FlashAttention (ES), section "El problema de la atención estándar";
+the same formula in FlashAttention (PT)): softmax(scale * Q K^T) V, with the
+full N x N score matrix S and probability matrix P materialised, here in
+float64. The pages list masking among the operations the fused kernel
+performs (FlashAttention (ES), "Fusión de operaciones en un único kernel") but
+do not say which masks; this reference takes the additive -inf reading:
+
+    s_ij    = scale * sum_k Q[i,k] K[j,k]
+    allowed = (j < key_len[b]) and (not causal or j <= i)
+    s_ij    = -inf where not allowed
+    m_i     = max_j s_ij,  e_ij = exp(s_ij - m_i),  l_i = sum_j e_ij
+    P_ij    = e_ij / l_i,  O_i = sum_j P_ij V_j,  LSE_i = m_i + log(l_i)
+
+A row with no allowed key gets O_i = 0 and LSE_i = -inf. key_len is clamped to
+[0, N]; None means every key is valid. LSE is the natural-log log-sum-exp of
+the allowed scaled logits, i.e. the running maximum and running sum of
+exponentials that the online softmax keeps (FlashAttention (ES), "Cálculo de
+Softmax en línea") folded into one number.
+
+Rows are processed in blocks of at most ``row_block`` full-width rows only to
+bound memory; each row's softmax still sees its whole row, so this is the
+plain definition and not a tiled algorithm.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def _as64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def allowed_mask(rows: np.ndarray, N: int, causal: bool, kl: int) -> np.ndarray:
+    """Boolean [len(rows), N]: which keys each query row may attend to."""
+    j = np.arange(N)[None, :]
+    ok = j < kl
+    if causal:
+        ok = ok & (j <= rows[:, None])
+    return ok
+
+
+def clamp_key_len(key_len, b: int, N: int) -> int:
+    if key_len is None:
+        return N
+    return int(min(max(int(key_len[b]), 0), N))
+
+
+def masked_scores(q_rows: np.ndarray, k: np.ndarray, scale: float, rows: np.ndarray,
+                  causal: bool, kl: int) -> np.ndarray:
+    """scale * q_rows @ k.T with -inf where the mask forbids the pair (float64)."""
+    s = float(scale) * (_as64(q_rows) @ _as64(k).T)
+    ok = allowed_mask(rows, k.shape[0], causal, kl)
+    return np.where(ok, s, -np.inf)
+
+
+def softmax_stats(s: np.ndarray):
+    """Row softmax of masked scores. Returns (P, m, l); fully masked rows give P=0."""
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])  # exp(-inf) = 0 at masked entries
+    l = e.sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(empty[:, None], 0.0, e / np.where(empty, 1.0, l)[:, None])
+    return p, m, l
+
+
+def _rows_forward(q_rows, k, v, scale, rows, causal, kl):
+    s = masked_scores(q_rows, k, scale, rows, causal, kl)
+    p, m, l = softmax_stats(s)
+    o = p @ _as64(v)
+    with np.errstate(divide="ignore"):
+        lse = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def attention_forward(q, k, v, scale: float, causal: bool = False,
+                      key_len: Optional[Sequence[int]] = None, row_block: int = 2048):
+    """O [B,H,N,d] and LSE [B,H,N] (float64) for inputs [B,H,N,d]."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        kl = clamp_key_len(key_len, b, N)
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                o[b, h, rows], lse[b, h, rows] = _rows_forward(
+                    q[b, h, rows], k[b, h], v[b, h], scale, rows, causal, kl)
+    return o, lse
+
+
+def attention_rows(q, k, v, scale: float, causal: bool, key_len, b: int, h: int,
+                   rows: Sequence[int]):
+    """O and LSE of selected query rows of one (b, h), each row against its full row."""
+    rows = np.asarray(rows, dtype=np.int64)
+    N = q.shape[2]
+    kl = clamp_key_len(key_len, b, N)
+    return _rows_forward(_as64(q[b, h, rows]), _as64(k[b, h]), _as64(v[b, h]), scale, rows,
+                         causal, kl)
+
+
+def probabilities(q, k, scale: float, causal: bool, key_len, b: int, h: int):
+    """The full N x N probability matrix P of one (b, h), for checks on P itself."""
+    N = q.shape[2]
+    rows = np.arange(N)
+    s = masked_scores(q[b, h], k[b, h], scale, rows, causal, clamp_key_len(key_len, b, N))
+    return softmax_stats(s)[0]

@@ -1,0 +1,319 @@
+"""Pins for the float64 oracle, checked against things other than itself.
+
+The pages print no worked numeric example, so every pin here is one of:
+arbitrary-precision brute force of the naive softmax formula, a second
+implementation (pure-Python two-pass loops), a library routine (torch's CPU
+scaled_dot_product_attention in float64), closed forms and invariants of the
+definition (FlashAttention (ES), "El problema de la atención estándar").
+"""
+import math
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as oatt
+
+mpmath.mp.dps = 50
+
+
+def rand_qkv(rng, B, H, N, d, scale_k=1.0):
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d)) * scale_k
+    v = rng.standard_normal((B, H, N, d))
+    return q, k, v
+
+
+def brute_force(q, k, v, scale, causal, key_len):
+    """exp(s)/sum(exp(s)) with no max subtraction, 50 significant digits."""
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    L = np.zeros((B, H, N))
+    for b in range(B):
+        kl = N if key_len is None else min(max(int(key_len[b]), 0), N)
+        for h in range(H):
+            for i in range(N):
+                allowed = [j for j in range(N) if j < kl and (not causal or j <= i)]
+                if not allowed:
+                    L[b, h, i] = -np.inf
+                    continue
+                w = {}
+                for j in allowed:
+                    s = mpmath.mpf(0)
+                    for t in range(d):
+                        s += mpmath.mpf(float(q[b, h, i, t])) * mpmath.mpf(float(k[b, h, j, t]))
+                    w[j] = mpmath.exp(mpmath.mpf(scale) * s)
+                z = mpmath.fsum(w.values())
+                for t in range(d):
+                    O[b, h, i, t] = float(mpmath.fsum(w[j] * mpmath.mpf(float(v[b, h, j, t]))
+                                                      for j in allowed) / z)
+                L[b, h, i] = float(mpmath.log(z))
+    return O, L
+
+
+def lse_close(a, b, tol):
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin)
+    assert np.all(a[~fin] == b[~fin])
+    if fin.any():
+        err = np.abs(a[fin] - b[fin]) / np.maximum(1.0, np.abs(b[fin]))
+        assert err.max() <= tol, err.max()
+
+
+CASES = [
+    # (N, d, causal, key_len mode)
+    (1, 1, False, None), (1, 4, True, None), (2, 3, True, None), (3, 8, False, "rand"),
+    (5, 2, True, "rand"), (8, 8, False, None), (13, 5, True, "rand"), (16, 8, True, None),
+    (16, 8, False, "rand"), (16, 4, True, "edge"),
+]
+
+
+@pytest.mark.parametrize("N,d,causal,klmode", CASES)
+def test_oracle_matches_bruteforce(N, d, causal, klmode):
+    rng = np.random.default_rng(1000 + N * 31 + d * 7 + causal)
+    B, H = 3, 2
+    q, k, v = rand_qkv(rng, B, H, N, d)
+    scale = 1.0 / math.sqrt(d) * 1.7
+    key_len = None
+    if klmode == "rand":
+        key_len = rng.integers(0, N + 1, size=B)
+    elif klmode == "edge":
+        key_len = np.array([0, 1, N + 5])  # empty, one key, clamped above N
+    O, L = oracle.attention_forward(q, k, v, scale, causal, key_len)
+    Ob, Lb = brute_force(q, k, v, scale, causal, key_len)
+    assert np.abs(O - Ob).max() <= 1e-13
+    lse_close(L, Lb, 1e-13)
+
+
+def test_fully_masked_rows_are_zero_and_neg_inf():
+    rng = np.random.default_rng(5)
+    q, k, v = rand_qkv(rng, 2, 2, 7, 3)
+    O, L = oracle.attention_forward(q, k, v, 0.5, True, np.array([0, 3]))
+    assert np.all(O[0] == 0) and np.all(L[0] == -np.inf)
+    assert np.all(np.isfinite(L[1]))
+
+
+def two_pass_loops(q, k, v, scale, causal, kl):
+    """Pure-Python safe softmax: pass 1 the row max, pass 2 exp-sum and normalise."""
+    N, d = len(q), len(q[0])
+    O = [[0.0] * d for _ in range(N)]
+    L = [-math.inf] * N
+    for i in range(N):
+        s = []
+        for j in range(N):
+            if j < kl and (not causal or j <= i):
+                s.append((j, scale * math.fsum(q[i][t] * k[j][t] for t in range(d))))
+        if not s:
+            continue
+        mx = max(x for _, x in s)
+        e = [(j, math.exp(x - mx)) for j, x in s]
+        z = math.fsum(x for _, x in e)
+        for t in range(d):
+            O[i][t] = math.fsum(w * v[j][t] for j, w in e) / z
+        L[i] = mx + math.log(z)
+    return np.array(O), np.array(L)
+
+
+@pytest.mark.parametrize("N,causal,kl", [(4, False, 4), (9, True, 9), (16, True, 11),
+                                         (16, False, 5), (12, False, 0)])
+def test_oracle_matches_two_pass_loops(N, causal, kl):
+    rng = np.random.default_rng(77 + N)
+    q, k, v = rand_qkv(rng, 1, 1, N, 6)
+    O, L = oracle.attention_forward(q, k, v, 0.4, causal, np.array([kl]))
+    O2, L2 = two_pass_loops(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.4, causal, kl)
+    assert np.abs(O[0, 0] - O2).max() <= 1e-14
+    lse_close(L[0, 0], L2, 1e-14)
+
+
+@pytest.mark.parametrize("N,d,causal,padded", [(33, 16, False, False), (64, 8, True, False),
+                                               (50, 32, False, True), (70, 16, True, True)])
+def test_oracle_matches_torch_sdpa_fp64(N, d, causal, padded):
+    rng = np.random.default_rng(900 + N)
+    B, H = 2, 3
+    q, k, v = rand_qkv(rng, B, H, N, d)
+    scale = 1.0 / math.sqrt(d)
+    key_len = rng.integers(1, N + 1, size=B) if padded else None
+    O, L = oracle.attention_forward(q, k, v, scale, causal, key_len)
+    j = torch.arange(N)
+    mask = torch.ones(B, 1, N, N, dtype=torch.bool)
+    if causal:
+        mask &= (j[None, :] <= j[:, None])[None, None]
+    if padded:
+        mask &= (j[None, None, None, :] < torch.as_tensor(key_len)[:, None, None, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=scale)
+    assert np.abs(O - ref.numpy()).max() <= 1e-12
+    # LSE by the library's own logsumexp over the same masked logits
+    s = torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2) * scale
+    s = s.masked_fill(~mask, -math.inf)
+    lse_close(L, torch.logsumexp(s, dim=-1).numpy(), 1e-13)
+
+
+def test_probability_rows_sum_to_one_and_mask_is_exact_zero():
+    rng = np.random.default_rng(3)
+    N = 40
+    q, k, _ = rand_qkv(rng, 1, 1, N, 8)
+    key_len = np.array([29])
+    P = oracle.probabilities(q, k, 0.7, True, key_len, 0, 0)
+    assert np.all(P >= 0)
+    assert np.abs(P.sum(axis=1) - 1).max() <= 1e-14
+    i, j = np.meshgrid(np.arange(N), np.arange(N), indexing="ij")
+    masked = (j > i) | (j >= 29)
+    assert np.all(P[masked] == 0.0)
+    assert np.all(P[~masked] > 0.0)
+
+
+def test_all_equal_keys_give_mean_of_allowed_values():
+    rng = np.random.default_rng(11)
+    N, d = 37, 5
+    q = rng.standard_normal((2, 1, N, d))
+    krow = rng.standard_normal(d)
+    k = np.broadcast_to(krow, (2, 1, N, d)).copy()
+    v = rng.standard_normal((2, 1, N, d))
+    scale = 0.3
+    key_len = np.array([N, 20])
+    O, L = oracle.attention_forward(q, k, v, scale, True, key_len)
+    for b, kl in enumerate(key_len):
+        for i in range(N):
+            n = min(i + 1, kl)
+            np.testing.assert_allclose(O[b, 0, i], v[b, 0, :n].mean(axis=0), rtol=0, atol=1e-14)
+            s = scale * float(q[b, 0, i] @ krow)
+            assert abs(L[b, 0, i] - (s + math.log(n))) <= 1e-13 * max(1, abs(s))
+
+
+def test_one_dominant_logit_selects_its_value_row():
+    rng = np.random.default_rng(12)
+    N, d = 64, 16
+    q, k, v = rand_qkv(rng, 1, 1, N, d)
+    i, jstar, c = 40, 17, 40.0
+    k[0, 0, jstar] = c * q[0, 0, i]
+    scale = 1.0 / 4.0
+    O, _ = oracle.attention_forward(q, k, v, scale, False, None)
+    s = scale * (k[0, 0] @ q[0, 0, i])
+    bound = 2 * np.abs(v).max() * np.exp(np.delete(s, jstar) - s[jstar]).sum()
+    assert bound < 1e-6
+    assert np.abs(O[0, 0, i] - v[0, 0, jstar]).max() <= bound
+
+
+def test_causal_row_zero_and_single_key():
+    rng = np.random.default_rng(13)
+    q, k, v = rand_qkv(rng, 2, 3, 19, 7)
+    O, L = oracle.attention_forward(q, k, v, 0.9, True, None)
+    assert np.array_equal(O[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(L[:, :, 0], 0.9 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                               rtol=1e-15, atol=1e-15)
+    q1, k1, v1 = rand_qkv(rng, 2, 2, 1, 9)
+    O1, L1 = oracle.attention_forward(q1, k1, v1, 0.2, False, None)
+    assert np.array_equal(O1, v1)
+    np.testing.assert_allclose(L1[..., 0], 0.2 * np.einsum("bhd,bhd->bh", q1[:, :, 0], k1[:, :, 0]),
+                               rtol=1e-15, atol=1e-15)
+
+
+def test_row_shift_invariance_via_key_offset():
+    """K -> K + 1 u^T adds scale*q_i.u to every logit of row i: O unchanged, LSE shifted."""
+    rng = np.random.default_rng(14)
+    q, k, v = rand_qkv(rng, 2, 2, 45, 8)
+    u = rng.standard_normal(8) * 3
+    key_len = np.array([45, 30])
+    O, L = oracle.attention_forward(q, k, v, 0.35, True, key_len)
+    O2, L2 = oracle.attention_forward(q, k + u, v, 0.35, True, key_len)
+    assert np.abs(O - O2).max() <= 1e-12
+    np.testing.assert_allclose(L2 - L, 0.35 * (q @ u), rtol=0, atol=1e-12)
+
+
+def test_linearity_in_values_and_constant_values():
+    rng = np.random.default_rng(15)
+    q, k, v1 = rand_qkv(rng, 1, 2, 30, 6)
+    v2 = rng.standard_normal(v1.shape)
+    A = rng.standard_normal((6, 6))
+    f = lambda v: oracle.attention_forward(q, k, v, 0.5, True, np.array([23]))[0]  # noqa: E731
+    assert np.abs(f(v1 + v2) - f(v1) - f(v2)).max() <= 1e-13
+    assert np.abs(f(v1 @ A) - f(v1) @ A).max() <= 1e-12
+    assert np.abs(f(np.ones_like(v1)) - 1.0).max() <= 1e-15
+
+
+def test_permutation_equivariance_without_mask():
+    rng = np.random.default_rng(16)
+    q, k, v = rand_qkv(rng, 1, 1, 25, 4)
+    O, L = oracle.attention_forward(q, k, v, 0.6, False, None)
+    pk = rng.permutation(25)
+    pq = rng.permutation(25)
+    O2, L2 = oracle.attention_forward(q[:, :, pq], k[:, :, pk], v[:, :, pk], 0.6, False, None)
+    assert np.abs(O2 - O[:, :, pq]).max() <= 1e-14
+    assert np.abs(L2 - L[:, :, pq]).max() <= 1e-13
+
+
+def test_huge_logits_stay_finite_and_exact():
+    """Scale 200: exp(s) overflows float64 without the max subtraction."""
+    rng = np.random.default_rng(17)
+    q, k, v = rand_qkv(rng, 1, 2, 12, 4)
+    O, L = oracle.attention_forward(q, k, v, 200.0, True, None)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    Ob, Lb = brute_force(q, k, v, 200.0, True, None)
+    assert np.abs(O - Ob).max() <= 1e-13
+    lse_close(L, Lb, 1e-14)
+
+
+def test_rows_api_matches_full():
+    rng = np.random.default_rng(18)
+    q, k, v = rand_qkv(rng, 2, 2, 90, 8)
+    key_len = np.array([90, 47])
+    O, L = oracle.attention_forward(q, k, v, 0.25, True, key_len, row_block=16)
+    rows = [0, 1, 46, 47, 89]
+    o, lse = oracle.attention_rows(q, k, v, 0.25, True, key_len, 1, 1, rows)
+    assert np.array_equal(o, O[1, 1, rows])
+    assert np.array_equal(lse, L[1, 1, rows])
+
+
+# --- the pins must catch plausible mistakes planted in the oracle -------------
+
+def _brute_check(monkeypatch_fn=None):
+    rng = np.random.default_rng(99)
+    q, k, v = rand_qkv(rng, 2, 2, 9, 4)
+    key_len = np.array([9, 6])
+    Ob, Lb = brute_force(q, k, v, 0.8, True, key_len)
+    O, L = oracle.attention_forward(q, k, v, 0.8, True, key_len)
+    return np.abs(O - Ob).max() <= 1e-13 and np.allclose(L, Lb, rtol=1e-13, atol=1e-13)
+
+
+MUTANTS = {
+    "strict_causal": lambda rows, N, causal, kl: (
+        (np.arange(N)[None, :] < kl) & (np.arange(N)[None, :] < rows[:, None])),
+    "key_len_off_by_one": lambda rows, N, causal, kl: (
+        (np.arange(N)[None, :] <= kl) & (np.arange(N)[None, :] <= rows[:, None])),
+    "mask_ignored": lambda rows, N, causal, kl: np.ones((len(rows), N), bool),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mask_mistakes(monkeypatch, name):
+    assert _brute_check()
+    monkeypatch.setattr(oatt, "allowed_mask", MUTANTS[name])
+    assert not _brute_check()
+
+
+def test_pins_catch_planted_arithmetic_mistakes(monkeypatch):
+    orig = oatt.masked_scores
+
+    def no_scale(q_rows, k, scale, rows, causal, kl):
+        return orig(q_rows, k, 1.0, rows, causal, kl)
+
+    def transposed(q_rows, k, scale, rows, causal, kl):
+        s = float(scale) * (np.asarray(k, np.float64) @ np.asarray(q_rows, np.float64).T)
+        return np.where(oatt.allowed_mask(rows, k.shape[0], causal, kl), s, -np.inf)
+
+    for bad in (no_scale, transposed):
+        monkeypatch.setattr(oatt, "masked_scores", bad)
+        assert not _brute_check()
+        monkeypatch.setattr(oatt, "masked_scores", orig)
+
+    orig_sm = oatt.softmax_stats
+
+    def log2_lse(s):
+        p, m, l = orig_sm(s)
+        return p, m, np.exp2(np.log(l))  # LSE would come out in the wrong base
+
+    monkeypatch.setattr(oatt, "softmax_stats", log2_lse)
+    assert not _brute_check()
