@@ -1,0 +1,92 @@
+"""Exact IO-aware attention forward for AMD Instinct MI355X (gfx950).
+
+Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` marshal torch
+tensors' device pointers and the current stream into the C entry points of the
+same names; ``forward`` additionally allocates O and LSE. Nothing here
+computes any part of the attention.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import FaError, abi_version, load, status_name  # noqa: F401
+
+_DTYPE = {
+    torch.float32: _lib.FA_DTYPE_FP32,
+    torch.float16: _lib.FA_DTYPE_FP16,
+    torch.bfloat16: _lib.FA_DTYPE_BF16,
+    torch.float8_e4m3fn: _lib.FA_DTYPE_FP8_E4M3,
+}
+
+
+def out_dtype(in_dtype: torch.dtype) -> torch.dtype:
+    return torch.bfloat16 if in_dtype == torch.float8_e4m3fn else in_dtype
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check_inputs(q, k, v, o, lse, key_len):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if o.shape != q.shape or o.dtype != out_dtype(q.dtype):
+        raise ValueError("o must be [B, H, N, d] of the output dtype")
+    if lse.shape != q.shape[:3] or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    if key_len is not None:
+        if (not key_len.is_cuda or key_len.dtype != torch.int32 or key_len.shape != (q.shape[0],)
+                or not key_len.is_contiguous()):
+            raise ValueError("key_len must be a contiguous device int32 tensor of shape [B]")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool = False,
+           key_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue fa_fwd on `stream` (default: torch's current stream)."""
+    _check_inputs(q, k, v, o, lse, key_len)
+    B, H, N, d = q.shape
+    _lib._check(_lib.fa_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale,
+                                causal, _ptr(key_len), _DTYPE[q.dtype], _stream(stream)))
+
+
+def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool = False,
+               key_len: Optional[torch.Tensor] = None, q_descale: float = 1.0,
+               k_descale: float = 1.0, v_descale: float = 1.0, stream=None) -> None:
+    """Enqueue fa_fwd_fp8 (per-tensor descaled fp8 e4m3 inputs, bf16 O)."""
+    if q8.dtype != torch.float8_e4m3fn:
+        raise ValueError("fa_fwd_fp8 takes float8_e4m3fn inputs")
+    _check_inputs(q8, k8, v8, o, lse, key_len)
+    B, H, N, d = q8.shape
+    _lib._check(_lib.fa_fwd_fp8_raw(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, H, N, d,
+                                    scale, causal, _ptr(key_len), q_descale, k_descale, v_descale,
+                                    _stream(stream)))
+
+
+def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
+            descale: Tuple[float, float, float] = (1.0, 1.0, 1.0),
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Allocate O and LSE on q's device and run the forward; returns (O, LSE)."""
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), dtype=out_dtype(q.dtype), device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.float8_e4m3fn:
+        fa_fwd_fp8(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
+    else:
+        fa_fwd(q, k, v, o, lse, scale, causal, key_len, stream=stream)
+    return o, lse

@@ -1,0 +1,106 @@
+// Host entry points of libfa: argument validation and dispatch.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// enqueues nothing and touches no buffer. The library allocates nothing and
+// keeps no state besides a per-thread description of the last error.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* what) {
+  snprintf(g_last_error, sizeof g_last_error, "%s", what);
+  return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool positive_finite(float x) { return isfinite(x) && x > 0.0f; }
+
+int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+            int d, float scale, int causal, const int32_t* key_len, int dtype, float qd, float kd,
+            float vd, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N and d must be >= 1");
+  if (dtype < FA_DTYPE_FP32 || dtype > FA_DTYPE_FP8_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "dtype is not a fa_dtype value");
+  if (!positive_finite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!positive_finite(qd) || !positive_finite(kd) || !positive_finite(vd))
+    return fail(FA_ERR_INVALID_ARG, "descales must be finite and > 0");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(FA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
+  if (!aligned(LSE, 4) || (key_len && !aligned(key_len, 4)))
+    return fail(FA_ERR_INVALID_ARG, "LSE and key_len must be 4-byte aligned");
+  // B*H*N*d elements, and the same count in bytes for fp32, must fit in int64.
+  const __int128 elems = (__int128)B * H * N * d;
+  if (elems * 4 > (__int128)INT64_MAX) return fail(FA_ERR_INVALID_ARG, "B*H*N*d overflows");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+
+  const fa::Kind kind = static_cast<fa::Kind>(dtype);
+  const int rows = fa::rows_per_block(kind, d);
+  fa::Params p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.key_len = key_len;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_qt = (N + rows - 1) / rows;
+  const long long grid = (long long)B * H * p.n_qt;
+  if (grid > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "B*H*ceil(N/rows) exceeds the grid limit");
+  p.scale_eff = scale * qd * kd;
+  if (!positive_finite(p.scale_eff)) return fail(FA_ERR_INVALID_ARG, "scale*q_descale*k_descale is not finite and > 0");
+  p.c = (float)((double)p.scale_eff * 1.4426950408889634);
+  p.o_scale = vd;
+
+  const hipError_t e = fa::launch_forward(kind, d, causal != 0, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+           int d, float scale, int causal, const int32_t* key_len, int dtype, void* stream) {
+  return forward(Q, K, V, O, LSE, B, H, N, d, scale, causal, key_len, dtype, 1.0f, 1.0f, 1.0f,
+                 stream);
+}
+
+int fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, void* O_bf16, float* LSE, int B,
+               int H, int N, int d, float scale, int causal, const int32_t* key_len,
+               float q_descale, float k_descale, float v_descale, void* stream) {
+  return forward(Q8, K8, V8, O_bf16, LSE, B, H, N, d, scale, causal, key_len, FA_DTYPE_FP8_E4M3,
+                 q_descale, k_descale, v_descale, stream);
+}
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

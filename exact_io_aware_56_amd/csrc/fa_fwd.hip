@@ -1,0 +1,688 @@
+// Fused exact attention forward for gfx950 (MI355X, CDNA4).
+//
+// One workgroup owns a tile of query rows of one (batch, head) and streams the
+// key/value tiles of that head through double-buffered LDS, keeping for every
+// query row a running maximum and a running sum of exponentials that are
+// corrected as each key tile arrives (FlashAttention (ES), "Tiling y
+// procesamiento por bloques" and "Cálculo de Softmax en línea"). QK^T, the
+// mask, the softmax and the product with V happen in this one kernel and only
+// O and the per-row log-sum-exp are written ("Fusión de operaciones en un
+// único kernel"). No N x N buffer exists.
+//
+// Matrix-core mapping (wave64, v_mfma_f32_32x32x16_{bf16,f16},
+// v_mfma_scale_f32_32x32x64_f8f6f4 and v_mfma_f32_32x32x2_f32):
+//
+//   Each wave owns 32 query rows and computes the transposed products
+//       S^T = K Q^T      (M = keys, N = queries, K = head dim)
+//       O^T += V^T P^T   (M = head dim, N = queries, K = keys)
+//   In the 32x32 accumulator layout lane l holds column l%32 and rows
+//   8*(i/4) + 4*(l/32) + i%4 of its 16 values, so with the queries as the
+//   column index every lane owns ONE query row: its 16 scores per 32-key
+//   block are that row's, the row maximum needs one exchange with lane
+//   l^32 (v_permlane32_swap), the rescale of O is a per-lane scalar, and
+//   the score accumulators feed P^T to the second product without leaving
+//   registers. The keys' order inside a 16-key reduction step is permuted by
+//   that layout; the V^T operand is read from LDS in the same permuted order
+//   with the gfx950 transposing LDS read (ds_read_b64_tr_b16), so no
+//   transposed copy of V is ever stored.
+//
+// Scores stay raw (unscaled) in registers; scale*log2(e) is folded into one
+// FMA ahead of v_exp_f32 (exp2), so exp(scale*s - m) = exp2(c*s - c*m).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// ---------------------------------------------------------------------------
+// Small wave-level helpers
+// ---------------------------------------------------------------------------
+
+// max / sum of x over lanes l and l^32 (the two halves hold the same query row)
+__device__ __forceinline__ float max_halves(float x) {
+  u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup -> (batch*head, query tile). Workgroups are handed to the XCDs
+// round-robin by id, so id % 8 names the XCD. Each XCD receives a contiguous
+// run of logical tiles (whole heads when B*H is a multiple of 8) so the
+// workgroups that run together on one XCD read the same head's K/V through
+// that XCD's L2. Causal tiles are issued longest-first (last query tile first)
+// so the short tiles fill the tail of the launch.
+__device__ __forceinline__ void map_block(int n_qt, bool causal, int& bh, int& qt) {
+  const int bid = blockIdx.x, total = gridDim.x;
+  int logical = bid;
+  if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+  bh = logical / n_qt;
+  const int r = logical - bh * n_qt;
+  qt = causal ? (n_qt - 1 - r) : r;
+}
+
+struct RowRange {
+  int bh, b, q_wg0, qw0, qrow, kl, nt, wnt;
+};
+
+// Which key tiles the workgroup streams (nt) and which of them this wave
+// multiplies (wnt): keys at or beyond key_len, and for causal keys beyond the
+// last row of the workgroup / wave, can only be masked, so those tiles are
+// skipped altogether.
+template <int BR, int BC, bool CAUSAL>
+__device__ __forceinline__ RowRange row_range(const Params& p, int wave, int l32) {
+  RowRange r;
+  int qt;
+  map_block(p.n_qt, CAUSAL, r.bh, qt);
+  r.b = r.bh / p.H;
+  const int N = p.N;
+  int kl = N;
+  if (p.key_len != nullptr) {
+    const int x = p.key_len[r.b];
+    kl = x < 0 ? 0 : (x > N ? N : x);
+  }
+  r.kl = kl;
+  r.q_wg0 = qt * BR;
+  r.qw0 = r.q_wg0 + wave * 32;
+  r.qrow = r.qw0 + l32;
+  int kv_end = kl;
+  if (CAUSAL) kv_end = min(kv_end, min(N, r.q_wg0 + BR));
+  r.nt = (kv_end + BC - 1) / BC;
+  int w_end = kv_end;
+  if (CAUSAL) w_end = min(w_end, r.qw0 + 32);
+  if (r.qw0 >= N) w_end = 0;
+  r.wnt = (w_end + BC - 1) / BC;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit element policies
+// ---------------------------------------------------------------------------
+struct Bf16 {
+  using T = __bf16;
+  using v8 = bf16x8;
+  using v4 = bf16x4;
+  static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4 tr4(const T* lds) {
+    return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)lds));
+  }
+  static __device__ __forceinline__ T cvt(float x) { return (T)x; }
+  // acc + sum of the 8 (already rounded) values, fp32 accumulation
+  static __device__ __forceinline__ float sum8(v8 x, float acc) {
+    const bf16x2 one = {(T)1.0f, (T)1.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[2 * k], x[2 * k + 1]}, one, acc, false);
+    return acc;
+  }
+};
+
+struct F16 {
+  using T = _Float16;
+  using v8 = f16x8;
+  using v4 = f16x4;
+  static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4 tr4(const T* lds) {
+    return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)lds));
+  }
+  static __device__ __forceinline__ T cvt(float x) { return (T)x; }
+  static __device__ __forceinline__ float sum8(v8 x, float acc) {
+    const f16x2 one = {(T)1.0f, (T)1.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc = __builtin_amdgcn_fdot2(f16x2{x[2 * k], x[2 * k + 1]}, one, acc, false);
+    return acc;
+  }
+};
+
+// Shared by the 16-bit and fp8 kernels: online-softmax update of one key
+// tile for this lane's query row, producing P^T operands in 16-bit.
+//   s[SB]  raw scores (masked entries already -inf)
+//   m, l   running max (raw units) and this lane's partial running sum
+//   o[DB]  output accumulators, rescaled here when the maximum grows
+template <class E, int SB, int DB>
+__device__ __forceinline__ void online_softmax(f32x16 (&s)[SB], float c, float& m, float& l,
+                                               f32x16 (&o)[DB],
+                                               typename E::v8 (&pf)[SB * 2]) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+  mx = max_halves(mx);
+  const float m_new = fmaxf(m, mx);
+  // Rescale only when some row of the wave saw a larger maximum; the result is
+  // identical either way, the branch only skips multiplications by 1.
+  if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+    const float alpha = (m_new > m) ? fast_exp2((m - m_new) * c) : 1.0f;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+  }
+  m = m_new;
+  const float base = (m == -INFINITY) ? 0.0f : -m * c;
+  // The running sum adds the same rounded P values that multiply V, so the
+  // weights applied to V's rows sum to one up to fp32 accumulation.
+  float rs = 0.0f;
+#pragma unroll
+  for (int ps = 0; ps < SB * 2; ++ps) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pf[ps][e] = E::cvt(fast_exp2(fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, base)));
+    rs = E::sum8(pf[ps], rs);
+  }
+  l += rs;
+}
+
+// Key index of accumulator element i of 32-key block sb for this lane half.
+__device__ __forceinline__ int acc_row(int sb, int i, int hi) {
+  return 32 * sb + 8 * (i >> 2) + 4 * hi + (i & 3);
+}
+
+template <int SB, bool CAUSAL>
+__device__ __forceinline__ void apply_mask(f32x16 (&s)[SB], int k0, int kl, int qrow, int hi) {
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + acc_row(sb, i, hi);
+      const bool ok = key < kl && (!CAUSAL || key <= qrow);
+      s[sb][i] = ok ? s[sb][i] : -INFINITY;
+    }
+}
+
+// O^T += V^T P^T for one key tile. V sits in LDS row-major [BC][VST] (16-bit);
+// the transposing read gives every lane 4 consecutive keys of one head-dim
+// column, matching the key order of the P^T operand (see acc_row).
+template <class E, int SB, int DB, int VST>
+__device__ __forceinline__ void pv_product(const typename E::T* vt, int lane,
+                                           const typename E::v8 (&pf)[SB * 2],
+                                           f32x16 (&o)[DB]) {
+  using v4 = typename E::v4;
+  using v8 = typename E::v8;
+  const int hi = lane >> 5;
+  const int row = 4 * hi + ((lane & 15) >> 2);
+  const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int ps = 0; ps < SB * 2; ++ps) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const typename E::T* base = vt + (16 * ps + row) * VST + 32 * db + col;
+      const v4 a0 = E::tr4(base);
+      const v4 a1 = E::tr4(base + 8 * VST);
+      const v8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = E::mma(a, pf[ps], o[db]);
+    }
+  }
+}
+
+// Final normalisation and the single write of O (16-bit) and LSE.
+template <class OutT, int D, int DB>
+__device__ __forceinline__ void epilogue(const Params& p, const RowRange& rr, int hi, float m,
+                                         float l, const f32x16 (&o)[DB]) {
+  typedef OutT v4 __attribute__((ext_vector_type(4)));
+  const float lt = sum_halves(l);
+  const bool live = lt > 0.0f;
+  const float inv = live ? p.o_scale / lt : 0.0f;
+  if (rr.qrow < p.N) {
+    OutT* orow = (OutT*)p.o + ((size_t)rr.bh * p.N + rr.qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        v4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (OutT)(o[db][4 * g + e] * inv);
+        *(v4*)(orow + 32 * db + 8 * g + 4 * hi) = out;
+      }
+    if (hi == 0)
+      p.lse[(size_t)rr.bh * p.N + rr.qrow] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel
+// ---------------------------------------------------------------------------
+template <class E, int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit(Params p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  constexpr int BR = NW * 32;
+  constexpr int KS = D / 16;   // reduction steps over the head dim in S^T
+  constexpr int SB = BC / 32;  // 32-key blocks per tile
+  constexpr int DB = D / 32;   // 32-wide head-dim blocks of O^T
+  constexpr int KST = D + 8;   // K row stride in LDS (elements): 16 B skew per row
+  constexpr int VST = D + 16;  // V row stride in LDS: 32 B skew per row
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int CH = BC * CPR / NT;
+  static_assert(BC * CPR % NT == 0, "tile must split evenly over the threads");
+
+  __shared__ __attribute__((aligned(16))) T ks[2][BC * KST];
+  __shared__ __attribute__((aligned(16))) T vs[2][BC * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
+  const int N = p.N;
+  const size_t head = (size_t)rr.bh * N * D;
+  const T* Kh = (const T*)p.k + head;
+  const T* Vh = (const T*)p.v + head;
+
+  // Q^T operand: lane holds query row qrow, head-dim 16*s + 8*hi .. +7.
+  v8 qf[KS];
+  {
+    const T* qr = (const T*)p.q + head + (size_t)rr.qrow * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (rr.qrow < N) qf[s] = *(const v8*)(qr + 16 * s);
+      else qf[s] = v8{};
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
+
+  // Keys at or beyond the streamed range are loaded as zeros so padded rows
+  // of V can never inject non-finite values through 0 * V.
+  const int kv_lim = min(rr.kl, rr.nt * BC);
+  i32x4 kreg[CH], vreg[CH];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * NT;
+      const int r = chunk / CPR, col = (chunk % CPR) * 8;
+      const int key = j * BC + r;
+      if (key < kv_lim) {
+        kreg[c] = *(const i32x4*)(Kh + (size_t)key * D + col);
+        vreg[c] = *(const i32x4*)(Vh + (size_t)key * D + col);
+      } else {
+        kreg[c] = i32x4{};
+        vreg[c] = i32x4{};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * NT;
+      const int r = chunk / CPR, col = (chunk % CPR) * 8;
+      *(i32x4*)(&ks[buf][r * KST + col]) = kreg[c];
+      *(i32x4*)(&vs[buf][r * VST + col]) = vreg[c];
+    }
+  };
+
+  if (rr.nt > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < rr.nt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < rr.nt) gload(j + 1);
+    if (j < rr.wnt) {
+      const T* kt = ks[buf];
+      f32x16 s[SB];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        s[sb] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const v8 a = *(const v8*)(kt + (32 * sb + l32) * KST + 16 * st + 8 * hi);
+          s[sb] = E::mma(a, qf[st], s[sb]);
+        }
+      }
+      const int k0 = j * BC;
+      if (k0 + BC > rr.kl || (CAUSAL && k0 + BC - 1 > rr.qw0))
+        apply_mask<SB, CAUSAL>(s, k0, rr.kl, rr.qrow, hi);
+      v8 pf[SB * 2];
+      online_softmax<E, SB, DB>(s, p.c, m, l, o, pf);
+      pv_product<E, SB, DB, VST>(vs[buf], lane, pf, o);
+    }
+    if (j + 1 < rr.nt) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<T, D, DB>(p, rr, hi, m, l, o);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 e4m3 kernel: S^T on the fp8 matrix cores (32x32x64), P V in bf16.
+// V's fp8 codes are widened to bf16 exactly when staged into LDS (every e4m3
+// value is a bf16 value), and P is rounded to bf16 as in the bf16 kernel.
+// ---------------------------------------------------------------------------
+
+// Four e4m3 codes -> four bf16 (exact): hardware fp8->f32 convert, keep the
+// high halves (an e4m3 value has at most 4 significant bits).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(unsigned w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2 r;
+  r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+  r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+  return r;
+}
+
+template <int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8(Params p) {
+  using E = Bf16;
+  using T8 = unsigned char;
+  constexpr int BR = NW * 32;
+  constexpr int KS = D / 64;   // 64-wide reduction steps in S^T
+  constexpr int SB = BC / 32;
+  constexpr int DB = D / 32;
+  constexpr int KST = D + 16;  // bytes per K row in LDS
+  constexpr int VST = D + 16;  // bf16 elements per V row in LDS
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 16;  // 16-byte (16-code) chunks per row
+  constexpr int CH = BC * CPR / NT;
+  static_assert(BC * CPR % NT == 0, "tile must split evenly over the threads");
+
+  __shared__ __attribute__((aligned(16))) T8 ks[2][BC * KST];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[2][BC * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
+  const int N = p.N;
+  const size_t head = (size_t)rr.bh * N * D;
+  const T8* Kh = (const T8*)p.k + head;
+  const T8* Vh = (const T8*)p.v + head;
+
+  // Q^T operand: lane holds query row qrow, head-dim 64*s + 32*hi .. +31.
+  i32x8 qf[KS];
+  {
+    const T8* qr = (const T8*)p.q + head + (size_t)rr.qrow * D + 32 * hi;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (rr.qrow < N) {
+        const i32x4 a = *(const i32x4*)(qr + 64 * s);
+        const i32x4 b = *(const i32x4*)(qr + 64 * s + 16);
+        qf[s] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        qf[s] = i32x8{};
+      }
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
+
+  const int kv_lim = min(rr.kl, rr.nt * BC);
+  i32x4 kreg[CH], vreg[CH];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * NT;
+      const int r = chunk / CPR, col = (chunk % CPR) * 16;
+      const int key = j * BC + r;
+      if (key < kv_lim) {
+        kreg[c] = *(const i32x4*)(Kh + (size_t)key * D + col);
+        vreg[c] = *(const i32x4*)(Vh + (size_t)key * D + col);
+      } else {
+        kreg[c] = i32x4{};
+        vreg[c] = i32x4{};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * NT;
+      const int r = chunk / CPR, col = (chunk % CPR) * 16;
+      *(i32x4*)(&ks[buf][r * KST + col]) = kreg[c];
+      i32x4 w0, w1;
+      u32x2 t;
+      t = fp8x4_to_bf16x4((unsigned)vreg[c][0]); w0[0] = t[0]; w0[1] = t[1];
+      t = fp8x4_to_bf16x4((unsigned)vreg[c][1]); w0[2] = t[0]; w0[3] = t[1];
+      t = fp8x4_to_bf16x4((unsigned)vreg[c][2]); w1[0] = t[0]; w1[1] = t[1];
+      t = fp8x4_to_bf16x4((unsigned)vreg[c][3]); w1[2] = t[0]; w1[3] = t[1];
+      *(i32x4*)(&vs[buf][r * VST + col]) = w0;
+      *(i32x4*)(&vs[buf][r * VST + col + 8]) = w1;
+    }
+  };
+
+  if (rr.nt > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < rr.nt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < rr.nt) gload(j + 1);
+    if (j < rr.wnt) {
+      const T8* kt = ks[buf];
+      f32x16 s[SB];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        s[sb] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const T8* ka = kt + (32 * sb + l32) * KST + 64 * st + 32 * hi;
+          const i32x4 a0 = *(const i32x4*)ka;
+          const i32x4 a1 = *(const i32x4*)(ka + 16);
+          const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+          // formats 0/0 = fp8 e4m3 for both operands; E8M0 scales 127 = 1.0
+          s[sb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[st], s[sb], 0, 0, 0, 127,
+                                                                  0, 127);
+        }
+      }
+      const int k0 = j * BC;
+      if (k0 + BC > rr.kl || (CAUSAL && k0 + BC - 1 > rr.qw0))
+        apply_mask<SB, CAUSAL>(s, k0, rr.kl, rr.qrow, hi);
+      bf16x8 pf[SB * 2];
+      online_softmax<E, SB, DB>(s, p.c, m, l, o, pf);
+      pv_product<E, SB, DB, VST>(vs[buf], lane, pf, o);
+    }
+    if (j + 1 < rr.nt) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<__bf16, D, DB>(p, rr, hi, m, l, o);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: both products on v_mfma_f32_32x32x2_f32 (full fp32 inputs, no
+// reduced-precision operand path), P kept in fp32.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
+  constexpr int BR = NW * 32;
+  constexpr int KS = D / 2;
+  constexpr int SB = BC / 32;
+  constexpr int DB = D / 32;
+  constexpr int KST = D + 1;  // odd stride: the 32 rows read per step hit 32 banks
+  constexpr int VST = D + 4;
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 4;
+  constexpr int CH = BC * CPR / NT;
+  static_assert(BC * CPR % NT == 0, "tile must split evenly over the threads");
+
+  __shared__ __attribute__((aligned(16))) float ks[2][BC * KST];
+  __shared__ __attribute__((aligned(16))) float vs[2][BC * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
+  const int N = p.N;
+  const size_t head = (size_t)rr.bh * N * D;
+  const float* Kh = (const float*)p.k + head;
+  const float* Vh = (const float*)p.v + head;
+
+  // Q^T operand: lane holds Q[qrow][2*s + hi]
+  float qf[KS];
+  {
+    const float* qr = (const float*)p.q + head + (size_t)rr.qrow * D + hi;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = rr.qrow < N ? qr[2 * s] : 0.0f;
+  }
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
+
+  const int kv_lim = min(rr.kl, rr.nt * BC);
+  i32x4 kreg[CH], vreg[CH];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * NT;
+      const int r = chunk / CPR, col = (chunk % CPR) * 4;
+      const int key = j * BC + r;
+      if (key < kv_lim) {
+        kreg[c] = *(const i32x4*)(Kh + (size_t)key * D + col);
+        vreg[c] = *(const i32x4*)(Vh + (size_t)key * D + col);
+      } else {
+        kreg[c] = i32x4{};
+        vreg[c] = i32x4{};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * NT;
+      const int r = chunk / CPR, col = (chunk % CPR) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ks[buf][r * KST + col + e] = __int_as_float(kreg[c][e]);
+      *(i32x4*)(&vs[buf][r * VST + col]) = vreg[c];
+    }
+  };
+
+  if (rr.nt > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < rr.nt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < rr.nt) gload(j + 1);
+    if (j < rr.wnt) {
+      const float* kt = ks[buf];
+      const float* vt = vs[buf];
+      f32x16 s[SB];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        s[sb] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[(32 * sb + l32) * KST + 2 * st + hi],
+                                                       qf[st], s[sb], 0, 0, 0);
+      }
+      const int k0 = j * BC;
+      if (k0 + BC > rr.kl || (CAUSAL && k0 + BC - 1 > rr.qw0))
+        apply_mask<SB, CAUSAL>(s, k0, rr.kl, rr.qrow, hi);
+      float mx = s[0][0];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m, mx);
+      if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+        const float alpha = (m_new > m) ? fast_exp2((m - m_new) * p.c) : 1.0f;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      m = m_new;
+      const float base = (m == -INFINITY) ? 0.0f : -m * p.c;
+      float rs = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[sb][i] = fast_exp2(fmaf(s[sb][i], p.c, base));
+          rs += s[sb][i];
+        }
+      l += rs;
+      // O^T += V^T P^T, one key per lane half per step, keys in accumulator order
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = acc_row(sb, i, hi);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[key * VST + 32 * db + l32], s[sb][i],
+                                                         o[db], 0, 0, 0);
+        }
+    }
+    if (j + 1 < rr.nt) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<float, D, DB>(p, rr, hi, m, l, o);
+}
+
+// ---------------------------------------------------------------------------
+// Launch table
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 4;  // 4 waves x 32 rows = 128 query rows per workgroup
+
+template <class K>
+hipError_t launch(K kernel, const Params& p, int threads, hipStream_t stream) {
+  const long long grid = (long long)p.B * p.H * p.n_qt;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  Params local = p;
+  void* args[] = {&local};
+  return hipLaunchKernel((const void*)kernel, dim3((unsigned)grid), dim3(threads), args, 0,
+                         stream);
+}
+
+template <int D, bool C>
+hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
+  constexpr int T = kWaves * 64;
+  switch (kind) {
+    case Kind::BF16: return launch(attn_fwd_16bit<Bf16, D, kWaves, 64, C>, p, T, s);
+    case Kind::F16: return launch(attn_fwd_16bit<F16, D, kWaves, 64, C>, p, T, s);
+    case Kind::FP8: return launch(attn_fwd_fp8<D, kWaves, 64, C>, p, T, s);
+    case Kind::F32: return launch(attn_fwd_f32<D, kWaves, 32, C>, p, T, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int rows_per_block(Kind, int d) { return (d == 64 || d == 128) ? kWaves * 32 : 0; }
+
+hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream) {
+  if (d == 64) return causal ? launch_d<64, true>(kind, p, stream) : launch_d<64, false>(kind, p, stream);
+  if (d == 128) return causal ? launch_d<128, true>(kind, p, stream) : launch_d<128, false>(kind, p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

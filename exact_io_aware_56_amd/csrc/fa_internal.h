@@ -1,0 +1,34 @@
+// Internal interface between the host entry points (fa_api.cpp) and the
+// kernel launchers (fa_fwd.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a kernel needs, passed by value as its only argument.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* key_len;  // NULL: every key valid
+  int B, H, N;
+  int n_qt;         // query tiles per head = ceil(N / rows per workgroup)
+  float c;          // scale_eff * log2(e): multiplies raw scores before exp2
+  float scale_eff;  // scale * q_descale * k_descale
+  float o_scale;    // v_descale
+};
+
+enum class Kind { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
+
+// Rows of Q owned by one workgroup for a (kind, d) pair; 0 if unsupported.
+int rows_per_block(Kind kind, int d);
+
+// Enqueue the forward on `stream`. Arguments are already validated and
+// p.n_qt filled in. Returns the launch's hipError_t.
+hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream);
+
+}  // namespace fa

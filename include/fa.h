@@ -1,0 +1,119 @@
+/*
+ * fa.h -- C ABI of libfa, the exact IO-aware attention forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (FlashAttention (ES), "El problema de la atención estándar"):
+ *
+ *     O   = softmax(scale * Q K^T + mask) V
+ *     LSE = per-row log-sum-exp of the masked, scaled logits (natural log)
+ *
+ * computed the way the pages' "Innovaciones clave" describe: Q, K and V are
+ * split into tiles held in on-chip memory, each query row keeps a running
+ * maximum and a running sum of exponentials that are corrected as new key
+ * tiles arrive (online softmax), QK^T, the mask, the softmax and the product
+ * with V are fused into one kernel, and only O and LSE are written. No N x N
+ * matrix exists anywhere, on the device or the host.
+ *
+ * Masks (the pages list masking as part of the fused kernel without saying
+ * which): the entry (i, j) of the logits is replaced by -inf unless
+ *     j < key_len[b]               (key padding; key_len NULL means N)
+ *     and (causal == 0 or j <= i)  (causal)
+ * A row with no allowed key yields O = 0 and LSE = -inf.
+ *
+ * Conventions shared by every entry point:
+ *   - Q, K, V, O are device pointers to dense row-major [B, H, N, d] tensors
+ *     (d fastest, then N, then H, then B), 16-byte aligned.
+ *   - LSE is a device pointer to float [B, H, N], 4-byte aligned.
+ *   - key_len is NULL or a device pointer to int32 [B]; values are clamped to
+ *     [0, N] on the device, so any int32 value is accepted.
+ *   - The caller owns every buffer. The library allocates no memory of any
+ *     kind and keeps no global state; calls are re-entrant and thread-safe.
+ *   - Calls are asynchronous: they enqueue work on `stream` (a hipStream_t;
+ *     NULL = the null stream) and return. Results are ready once the stream
+ *     is synchronised. A fault inside the kernel surfaces at the caller's
+ *     next synchronisation, not as a return value.
+ *   - Errors are returned as fa_status codes, never by aborting. Argument
+ *     checks run on the host before any HIP call; on an argument error no
+ *     device work is enqueued and no buffer is touched.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
+  FA_DTYPE_FP16 = 1,     /* IEEE half in, half out                           */
+  FA_DTYPE_BF16 = 2,     /* bfloat16 in, bfloat16 out                        */
+  FA_DTYPE_FP8_E4M3 = 3  /* OCP fp8 e4m3 ("fn", max 448) in, bfloat16 out    */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* a NULL or misaligned pointer, a size < 1, an
+                              out-of-range dtype, a scale or descale that is
+                              not finite and > 0, or sizes whose products
+                              overflow                                      */
+  FA_ERR_UNSUPPORTED = -2, /* a head dimension d other than 64 or 128       */
+  FA_ERR_HIP = -3          /* the HIP runtime refused the launch            */
+} fa_status;
+
+/*
+ * fa_fwd -- attention forward for one batch of B x H heads.
+ *
+ *   Q, K, V  [in]  device, [B,H,N,d] of `dtype` (fp8 e4m3 when dtype == 3)
+ *   O        [out] device, [B,H,N,d]; of `dtype`, or bfloat16 for fp8 input
+ *   LSE      [out] device, float [B,H,N], natural-log log-sum-exp per row
+ *   B, H, N  batch, heads, sequence length (queries and keys), each >= 1
+ *   d        head dimension; 64 or 128
+ *   scale    multiplies QK^T before the mask; finite and > 0 (the pages use
+ *            1/sqrt(d))
+ *   causal   0 or 1 (any non-zero value means 1)
+ *   key_len  NULL or device int32 [B] (see above)
+ *   dtype    a fa_dtype value; fp8 input here means descales of 1.0
+ *   stream   hipStream_t the work is enqueued on
+ *
+ * Returns FA_OK once the kernel is enqueued, or a negative fa_status.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int H, int N, int d, float scale, int causal,
+           const int32_t* key_len, int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- fa_fwd for fp8 e4m3 inputs quantised per tensor.
+ *
+ * The stored codes Q8, K8, V8 represent Q = q_descale * Q8, K = k_descale *
+ * K8 and V = v_descale * V8. The logits are scale * q_descale * k_descale *
+ * (Q8 K8^T); O = v_descale * softmax(...) V8, written as bfloat16. Both
+ * matrix products accumulate in fp32. The descales must be finite and > 0.
+ * fa_fwd(..., FA_DTYPE_FP8_E4M3, ...) equals this call with descales 1.0.
+ * Arguments otherwise as fa_fwd.
+ */
+int fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, void* O_bf16, float* LSE,
+               int B, int H, int N, int d, float scale, int causal,
+               const int32_t* key_len, float q_descale, float k_descale,
+               float v_descale, void* stream);
+
+/* A static, human-readable name for a fa_status value (never NULL). */
+const char* fa_status_str(int status);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+/*
+ * A static description of the last error returned on the calling thread
+ * (which argument was rejected, or the HIP error string); "" after FA_OK.
+ */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */
