@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one fa_fwd call over the whole workload (every head, every query
+tile: the full hot path). The default workload is the long-context causal
+decoder attention the headline metric is quoted on: bf16, B=1, H=32,
+N=8192, d=128, causal, 1% of the key rows scaled x8, scale 1/sqrt(128).
+
+Prints ONE JSON line. `value` is attention TFLOP/s (4*B*H*N^2*d, halved for
+causal) over the timed steps with inputs already in HBM; `roofline` prices the
+kernel's per-launch average (HIP events on the launch stream) against the
+dense bf16 MFMA peak; `cpu_baseline` times the float64 oracle on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MFMA peak, bf16 causal B1 H32 N8192 d128"
+# Published dense MI355X peaks (TFLOP/s) per input dtype of the contraction.
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp32": 157.3}
+KERNEL_SOURCES = ["exact_io_aware_56_amd/csrc/fa_fwd.hip", "exact_io_aware_56_amd/csrc/fa_api.cpp",
+                  "exact_io_aware_56_amd/csrc/fa_internal.h"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sha():
+        return None
+    return float(val.group(1))
+
+
+def algorithmic_bytes(spec) -> int:
+    """Q, K, V read once, O written once, LSE written once."""
+    e_in = {"fp32": 4, "fp16": 2, "bf16": 2, "fp8": 1}[spec.dtype]
+    e_out = {"fp32": 4, "fp16": 2, "bf16": 2, "fp8": 2}[spec.dtype]
+    n = spec.B * spec.H * spec.N * spec.d
+    return (3 * e_in + e_out) * n + 4 * spec.B * spec.H * spec.N
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the float64 oracle on whole heads of the workload until the budget
+    is spent (at least one head); returns the JSON object."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i["num_threads"] for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    s = w.spec
+    q, k, v = w.exact()
+    kl = w.key_len_or_none()
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(s.B):
+        for h in range(s.H):
+            kb = None if kl is None else kl[b:b + 1]
+            oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
+                                     v[b:b + 1, h:h + 1], s.scale, s.causal, kb)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = s.flops() / (s.B * s.H) * heads
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {s.B * s.H} heads of the same workload, every query row, "
+                      f"float64, {dt:.2f} s wall"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_causal_bf16")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the cpu_baseline leg (0 disables)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; "
+                                   "multi-GPU runs are not supported (use --gpus 1)"}))
+        return 2
+
+    import torch
+
+    import exact_io_aware_56_amd as fa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 3
+    spec = W.SPECS[args.workload]
+    w = W.draw(spec)
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    kl = None if w.key_len is None else torch.from_numpy(w.key_len).to(dev)
+    o = torch.empty(q.shape, dtype=fa.out_dtype(q.dtype), device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if spec.dtype == "fp8":
+            fa.fa_fwd_fp8(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
+        else:
+            fa.fa_fwd(q, k, v, o, lse, spec.scale, spec.causal, kl, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(o.float()).all()):
+        print(json.dumps({"error": "non-finite output"}))
+        return 4
+
+    # Per-launch events on the launch stream, plus the outer bracket.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    outer0, outer1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    outer0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    outer1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    total_ms = outer0.elapsed_time(outer1)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_launch_ms = sum(per) / len(per)
+    ms_per_step = total_ms / args.steps
+
+    flop = spec.flops()
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[spec.dtype]
+    achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic(spec.name)
+    result = {
+        "metric": METRIC if spec.name == "long_causal_bf16" else
+        f"attention fwd TFLOP/s ({spec.name})",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape and structure)",
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "config": {
+            "workload": spec.name, "B": spec.B, "H": spec.H, "N": spec.N, "d": spec.d,
+            "causal": spec.causal, "scale": spec.scale,
+            "key_len": None if w.key_len is None else "per-batch padding",
+            "outlier_keys_frac": spec.outlier_frac, "seed": spec.seed,
+            "launch_ms_p10": round(per[len(per) // 10], 5),
+            "launch_ms_median": round(per[len(per) // 2], 5),
+            "launch_ms_p90": round(per[(9 * len(per)) // 10], 5),
+            "host_wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": algorithmic_bytes(spec),
+            "kernel_sources_sha256_16": kernel_sha(),
+        },
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

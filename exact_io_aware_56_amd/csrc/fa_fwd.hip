@@ -70,6 +70,33 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resource (gfx9 descriptor word 3) over `bytes` bytes at `base`.
+// Loads at offsets >= bytes return zeros without touching memory, which is how
+// ragged tails and padded keys are zero-filled with no branches.
+// Both arguments must be wave-uniform; readfirstlane states that to the
+// compiler so the descriptor lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
+// Resource over key rows [j*BC, j*BC + BC) of one head, cut at row `limit`.
+// A tile wholly past the limit gets an empty range (and the head's base).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* head, int j, int BC,
+                                                            int limit, int row_bytes) {
+  const int rows = max(0, min(BC, limit - j * BC));
+  const char* base = (const char*)head + (rows > 0 ? (size_t)j * BC * row_bytes : 0);
+  return buffer_rsrc(base, rows * row_bytes);
+}
+
+__device__ __forceinline__ i32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // Workgroup -> (batch*head, query tile). Workgroups are handed to the XCDs
 // round-robin by id, so id % 8 names the XCD. Each XCD receives a contiguous
 // run of logical tiles (whole heads when B*H is a multiple of 8) so the
@@ -291,7 +318,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit(Params p) {
   __shared__ __attribute__((aligned(16))) T ks[2][BC * KST];
   __shared__ __attribute__((aligned(16))) T vs[2][BC * VST];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
@@ -300,14 +328,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit(Params p) {
   const T* Vh = (const T*)p.v + head;
 
   // Q^T operand: lane holds query row qrow, head-dim 16*s + 8*hi .. +7.
+  // Rows at or beyond N read as zeros.
   v8 qf[KS];
   {
-    const T* qr = (const T*)p.q + head + (size_t)rr.qrow * D + 8 * hi;
+    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, D * (int)sizeof(T));
+    const int off = ((rr.qrow - rr.q_wg0) * D + 8 * hi) * (int)sizeof(T);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (rr.qrow < N) qf[s] = *(const v8*)(qr + 16 * s);
-      else qf[s] = v8{};
-    }
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
   }
 
   f32x16 o[DB];
@@ -315,23 +342,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit(Params p) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.0f;
 
-  // Keys at or beyond the streamed range are loaded as zeros so padded rows
-  // of V can never inject non-finite values through 0 * V.
-  const int kv_lim = min(rr.kl, rr.nt * BC);
+  // Keys at or beyond key_len are loaded as zeros (so padded rows of V can
+  // never inject non-finite values through 0 * V); so is the tile past the
+  // last one, which the loop prefetches unconditionally.
+  const int kv_lim = rr.kl;
   i32x4 kreg[CH], vreg[CH];
   auto gload = [&](int j) {
+    const auto rk = tile_rsrc(Kh, j, BC, kv_lim, D * (int)sizeof(T));
+    const auto rv = tile_rsrc(Vh, j, BC, kv_lim, D * (int)sizeof(T));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int chunk = tid + c * NT;
-      const int r = chunk / CPR, col = (chunk % CPR) * 8;
-      const int key = j * BC + r;
-      if (key < kv_lim) {
-        kreg[c] = *(const i32x4*)(Kh + (size_t)key * D + col);
-        vreg[c] = *(const i32x4*)(Vh + (size_t)key * D + col);
-      } else {
-        kreg[c] = i32x4{};
-        vreg[c] = i32x4{};
-      }
+      const int off = ((chunk / CPR) * D + (chunk % CPR) * 8) * (int)sizeof(T);
+      kreg[c] = load16(rk, off);
+      vreg[c] = load16(rv, off);
     }
   };
   auto sstore = [&](int buf) {
@@ -344,14 +368,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit(Params p) {
     }
   };
 
-  if (rr.nt > 0) {
-    gload(0);
-    sstore(0);
-  }
+  gload(0);
+  sstore(0);
   __syncthreads();
   for (int j = 0; j < rr.nt; ++j) {
     const int buf = j & 1;
-    if (j + 1 < rr.nt) gload(j + 1);
+    gload(j + 1);
     if (j < rr.wnt) {
       const T* kt = ks[buf];
       f32x16 s[SB];
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit(Params p) {
       online_softmax<E, SB, DB>(s, p.c, m, l, o, pf);
       pv_product<E, SB, DB, VST>(vs[buf], lane, pf, o);
     }
-    if (j + 1 < rr.nt) sstore(buf ^ 1);
+    sstore(buf ^ 1);
     __syncthreads();
   }
   epilogue<T, D, DB>(p, rr, hi, m, l, o);
@@ -412,7 +434,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8(Params p) {
   __shared__ __attribute__((aligned(16))) T8 ks[2][BC * KST];
   __shared__ __attribute__((aligned(16))) __bf16 vs[2][BC * VST];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
@@ -423,16 +446,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8(Params p) {
   // Q^T operand: lane holds query row qrow, head-dim 64*s + 32*hi .. +31.
   i32x8 qf[KS];
   {
-    const T8* qr = (const T8*)p.q + head + (size_t)rr.qrow * D + 32 * hi;
+    const auto rq = tile_rsrc((const T8*)p.q + head, rr.q_wg0 / BR, BR, N, D);
+    const int off = (rr.qrow - rr.q_wg0) * D + 32 * hi;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (rr.qrow < N) {
-        const i32x4 a = *(const i32x4*)(qr + 64 * s);
-        const i32x4 b = *(const i32x4*)(qr + 64 * s + 16);
-        qf[s] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-      } else {
-        qf[s] = i32x8{};
-      }
+      const i32x4 a = load16(rq, off + 64 * s);
+      const i32x4 b = load16(rq, off + 64 * s + 16);
+      qf[s] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
 
@@ -441,21 +461,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8(Params p) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.0f;
 
-  const int kv_lim = min(rr.kl, rr.nt * BC);
+  const int kv_lim = rr.kl;
   i32x4 kreg[CH], vreg[CH];
   auto gload = [&](int j) {
+    const auto rk = tile_rsrc(Kh, j, BC, kv_lim, D);
+    const auto rv = tile_rsrc(Vh, j, BC, kv_lim, D);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int chunk = tid + c * NT;
-      const int r = chunk / CPR, col = (chunk % CPR) * 16;
-      const int key = j * BC + r;
-      if (key < kv_lim) {
-        kreg[c] = *(const i32x4*)(Kh + (size_t)key * D + col);
-        vreg[c] = *(const i32x4*)(Vh + (size_t)key * D + col);
-      } else {
-        kreg[c] = i32x4{};
-        vreg[c] = i32x4{};
-      }
+      const int off = (chunk / CPR) * D + (chunk % CPR) * 16;
+      kreg[c] = load16(rk, off);
+      vreg[c] = load16(rv, off);
     }
   };
   auto sstore = [&](int buf) {
@@ -475,14 +491,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8(Params p) {
     }
   };
 
-  if (rr.nt > 0) {
-    gload(0);
-    sstore(0);
-  }
+  gload(0);
+  sstore(0);
   __syncthreads();
   for (int j = 0; j < rr.nt; ++j) {
     const int buf = j & 1;
-    if (j + 1 < rr.nt) gload(j + 1);
+    gload(j + 1);
     if (j < rr.wnt) {
       const T8* kt = ks[buf];
       f32x16 s[SB];
@@ -507,7 +521,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8(Params p) {
       online_softmax<E, SB, DB>(s, p.c, m, l, o, pf);
       pv_product<E, SB, DB, VST>(vs[buf], lane, pf, o);
     }
-    if (j + 1 < rr.nt) sstore(buf ^ 1);
+    sstore(buf ^ 1);
     __syncthreads();
   }
   epilogue<__bf16, D, DB>(p, rr, hi, m, l, o);
@@ -533,7 +547,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
   __shared__ __attribute__((aligned(16))) float ks[2][BC * KST];
   __shared__ __attribute__((aligned(16))) float vs[2][BC * VST];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
@@ -544,30 +559,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
   // Q^T operand: lane holds Q[qrow][2*s + hi]
   float qf[KS];
   {
-    const float* qr = (const float*)p.q + head + (size_t)rr.qrow * D + hi;
+    const auto rq = tile_rsrc((const float*)p.q + head, rr.q_wg0 / BR, BR, N, D * 4);
+    const int off = ((rr.qrow - rr.q_wg0) * D + hi) * 4;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = rr.qrow < N ? qr[2 * s] : 0.0f;
+    for (int s = 0; s < KS; ++s)
+      qf[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rq, off + 8 * s, 0, 0));
   }
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.0f;
 
-  const int kv_lim = min(rr.kl, rr.nt * BC);
+  const int kv_lim = rr.kl;
   i32x4 kreg[CH], vreg[CH];
   auto gload = [&](int j) {
+    const auto rk = tile_rsrc(Kh, j, BC, kv_lim, D * 4);
+    const auto rv = tile_rsrc(Vh, j, BC, kv_lim, D * 4);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int chunk = tid + c * NT;
-      const int r = chunk / CPR, col = (chunk % CPR) * 4;
-      const int key = j * BC + r;
-      if (key < kv_lim) {
-        kreg[c] = *(const i32x4*)(Kh + (size_t)key * D + col);
-        vreg[c] = *(const i32x4*)(Vh + (size_t)key * D + col);
-      } else {
-        kreg[c] = i32x4{};
-        vreg[c] = i32x4{};
-      }
+      const int off = ((chunk / CPR) * D + (chunk % CPR) * 4) * 4;
+      kreg[c] = load16(rk, off);
+      vreg[c] = load16(rv, off);
     }
   };
   auto sstore = [&](int buf) {
@@ -581,14 +594,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
     }
   };
 
-  if (rr.nt > 0) {
-    gload(0);
-    sstore(0);
-  }
+  gload(0);
+  sstore(0);
   __syncthreads();
   for (int j = 0; j < rr.nt; ++j) {
     const int buf = j & 1;
-    if (j + 1 < rr.nt) gload(j + 1);
+    gload(j + 1);
     if (j < rr.wnt) {
       const float* kt = ks[buf];
       const float* vt = vs[buf];
@@ -642,7 +653,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
                                                          o[db], 0, 0, 0);
         }
     }
-    if (j + 1 < rr.nt) sstore(buf ^ 1);
+    sstore(buf ^ 1);
     __syncthreads();
   }
   epilogue<float, D, DB>(p, rr, hi, m, l, o);
