@@ -105,6 +105,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="long_causal_bf16")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times) and exit; "
+                         "its HBM counters calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -120,6 +123,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         return 3
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return 0
     spec = W.SPECS[args.workload]
     w = W.draw(spec)
     dev = torch.device("cuda", 0)

@@ -35,18 +35,22 @@ def run(cmd):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(extra_flags=(), lib: str = LIB, obj_dir: str = OUT_DIR) -> str:
+    """Compile and link libfa.so. `extra_flags` (e.g. -DFA_KEY_TILE=32) reach
+    the kernel compile only; `lib` / `obj_dir` redirect the outputs."""
+    os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
-    kern_o = os.path.join(OUT_DIR, "fa_fwd.o")
-    api_o = os.path.join(OUT_DIR, "fa_api.o")
-    run([cc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c",
+    kern_o = os.path.join(obj_dir, "fa_fwd.o")
+    api_o = os.path.join(obj_dir, "fa_api.o")
+    run([cc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *extra_flags, "-x", "hip", "-c",
          os.path.join(CSRC, "fa_fwd.hip"), "-o", kern_o])
     run([cc, *COMMON, "-c", os.path.join(CSRC, "fa_api.cpp"), "-o", api_o])
-    tmp = LIB + ".tmp"
-    run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kern_o, api_o, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    # -z defs: an unresolved symbol (e.g. a kernel handle the host pass failed
+    # to emit) fails the link instead of the first dlopen
+    run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", kern_o, api_o, "-o", tmp])
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -68,6 +68,34 @@ def test_fp32_outlier_keys():
         assert same_inf and mx <= 4e-5 and mean <= 1e-6 and dl <= 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp8", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_keeps_growing(dtype, causal):
+    """Keys scaled up along the sequence so every key tile raises the row
+    maxima, by small and by very large steps: the running-max correction
+    (and its threshold) must reproduce the exact softmax."""
+    d = 128 if dtype == "fp8" else 64
+    spec = small_spec(dtype, d, 700, causal, True, B=2, H=2, seed=8300 + causal, outliers=False)
+    w = W.draw(spec)
+    grow = torch.linspace(0.2, 6.0, spec.N).reshape(1, 1, spec.N, 1)
+    if dtype == "fp8":
+        k = (w.k.to(torch.float32) * grow).clamp(-448, 448)
+        w.k = k.to(torch.float8_e4m3fn)
+    else:
+        w.k = (w.k.to(torch.float32) * grow).to(w.k.dtype)
+    say(f"case growing logits dtype={dtype} causal={causal}")
+    o, lse = run(w)
+    o_ref, lse_ref = full_oracle(w)
+    if dtype == "fp32":
+        # logits up to ~40: the fp32 dot-product bar of test_fp32_outlier_keys
+        from parity import errors
+        mx, mean, dl, same_inf = errors(o, lse, o_ref, lse_ref, True)
+        say(f"  max|dO|={mx:.3e} mean|dO|={mean:.3e} max|dLSE|={dl:.3e}")
+        assert same_inf and mx <= 4e-5 and mean <= 1e-6 and dl <= 1e-5
+    else:
+        assert_close(o, lse, o_ref, lse_ref, dtype, "growing")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp32", "fp16"])
 def test_degenerate_key_lengths(dtype):
     """key_len 0 (no key: O = 0, LSE = -inf), 1, negative and above N (clamped)."""
