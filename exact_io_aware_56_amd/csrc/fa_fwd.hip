@@ -75,20 +75,17 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_WAVES_PER_EU
 #define FA_WAVES_PER_EU 2
 #endif
-#ifndef FA_PIPE
-#define FA_PIPE 0  // 16-bit kernel: 0 simple, 1 pipelined, 2 ping-pong, 3 two row groups per wave
+#ifndef FA_16BIT_KERNEL
+#define FA_16BIT_KERNEL 1  // 16-bit inputs: 0 register-staged kernel, 1 direct-to-LDS kernel
 #endif
-#ifndef FA_SCHED
-#define FA_SCHED 1  // explicit MFMA / VALU / LDS interleave in the pipelined kernel
+#ifndef FA_DMA_WAVES
+#define FA_DMA_WAVES 4  // waves per workgroup of the direct-to-LDS kernel
 #endif
-#ifndef FA_RESCALE_ALWAYS
-#define FA_RESCALE_ALWAYS 0  // 1: multiply O by the correction on every tile, branch-free
+#ifndef FA_NBUF
+#define FA_NBUF 2  // LDS buffers per operand in the direct-to-LDS kernel (2 or 3)
 #endif
 #ifndef FA_LOOKAHEAD
-#define FA_LOOKAHEAD 3  // LDS operand reads issued this many MFMAs ahead (ping-pong kernel)
-#endif
-#ifndef FA_SCHED_VALU
-#define FA_SCHED_VALU 6  // VALU instructions placed after each score MFMA
+#define FA_LOOKAHEAD 2  // LDS operand reads issued this many MFMAs ahead
 #endif
 
 // ---------------------------------------------------------------------------
@@ -106,6 +103,15 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Returns x unchanged, but through an asm statement the optimizer cannot look
+// into or move. Used inside the rarely taken O-rescale branches: without it
+// the compiler hoists the (speculatable) multiplies of O above the branch and
+// executes them on every tile.
+__device__ __forceinline__ float pinned(float x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
 
 // Raw buffer resource (gfx9 descriptor word 3) over `bytes` bytes at `base`.
 // Loads at offsets >= bytes return zeros without touching memory, which is how
@@ -263,7 +269,7 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[SB], float c, float t
   mx = max_halves(mx);
   const bool move = mx > m + thr;  // true on the first live tile (m = -inf)
   if (__builtin_amdgcn_ballot_w64(move) != 0) {
-    const float alpha = move ? fast_exp2((m - mx) * c) : 1.0f;  // exp2(-inf) = 0
+    const float alpha = pinned(move ? fast_exp2((m - mx) * c) : 1.0f);  // exp2(-inf) = 0
     l *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -462,19 +468,10 @@ __global__ __launch_bounds__(NW * 64, FA_WAVES_PER_EU) void attn_fwd_16bit(Param
 }
 
 // ---------------------------------------------------------------------------
-// bf16 / fp16 kernel, software-pipelined (the default for 16-bit inputs)
-//
-// K and V tiles are copied HBM -> LDS by the direct-to-LDS buffer loads of
-// gfx950 (buffer_load_dwordx4 ... lds, 16 bytes per lane): no staging
-// registers and no LDS write instructions. Rows are stored unpadded and the
-// 16-byte slots of each row are XOR-permuted (k_swz / v_swz) so the operand
-// reads below are free of bank conflicts.
-//
-// Each wave keeps two score tiles in flight: while the VALU computes the
-// online softmax of key tile j, the matrix cores already compute the scores
-// of tile j+1, and then P_j V_j. For that, LDS holds K one tile ahead of V:
-// during iteration j it holds K_{j+1} and V_j while the copies of K_{j+2} and
-// V_{j+1} land in the two other buffers; one barrier per iteration.
+// Direct-to-LDS tile copies (gfx950 buffer_load_dwordx4 ... lds, 16 bytes per
+// lane): no staging registers and no LDS write instructions. Rows are stored
+// unpadded and the 16-byte slots of each row are XOR-permuted so that the
+// operand reads of the kernels below are free of bank conflicts.
 // ---------------------------------------------------------------------------
 
 // Slot permutations (16-byte slots, row = D*2 bytes). k_swz keeps the 16 rows
@@ -500,415 +497,33 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rs, unsigned c
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// Instruction order for one pipelined iteration (after the rescale branch):
-// each next-tile score MFMA is preceded by its K operand read and followed by
-// a slice of the softmax VALU work; each P V MFMA by its two V reads.
-// (Group masks: 0x008 MFMA, 0x002 VALU, 0x100 LDS read.)
-template <int NS, int NPV>
-__device__ __forceinline__ void interleave() {
-#if FA_SCHED
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, FA_SCHED_VALU, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < NPV; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-  }
-#endif
+// s_waitcnt vmcnt(N): all but the N most recent vector-memory loads are done
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt / lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <class E, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, FA_WAVES_PER_EU) void attn_fwd_16bit_pipe(Params p) {
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel (the default for 16-bit inputs)
+//
+// NW waves per workgroup (32 query rows each), two workgroups per CU at
+// NW = 4. K and V tiles reach LDS through the direct-to-LDS copies above,
+// NBUF buffers deep: the copy of tile j + NBUF - 1 lands while tile j is used.
+// Within a tile every MFMA's LDS operand is read kLookahead MFMAs ahead
+// through a small ring of registers, and the first V operands of O += P V are
+// read before the softmax arithmetic so that it hides their latency. The LDS
+// operand reads and their latency in front of each MFMA, not the arithmetic,
+// bound the register-staged kernel above; this one trims them.
+// ---------------------------------------------------------------------------
+template <class E, int D, int BC, int NW, int NBUF, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using v4 = typename E::v4;
   constexpr int BR = NW * 32;
-  constexpr int KS = D / 16;   // reduction steps over the head dim in S^T
-  constexpr int SB = BC / 32;  // 32-key blocks per tile
-  constexpr int DB = D / 32;   // 32-wide head-dim blocks of O^T
-  constexpr int PS = BC / 16;  // reduction steps over keys in O^T
-  constexpr int RB = D * 2;    // bytes per K / V row
-  constexpr int CPR = D / 8;   // 16-byte slots per row
-  constexpr int TB = BC * RB;  // bytes per K or V tile
-  constexpr int NDMA = TB / (1024 * NW);  // 1 KB direct-to-LDS copies per wave per tile
-  static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB copies per wave");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
-  const int N = p.N;
-  const size_t head = (size_t)rr.bh * N * D;
-  const T* Kh = (const T*)p.k + head;
-  const T* Vh = (const T*)p.v + head;
-
-  v8 qf[KS];
-  {
-    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, RB);
-    const int off = ((rr.qrow - rr.q_wg0) * D + 8 * hi) * 2;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
-  }
-
-  // Per-lane LDS byte offsets of the operand reads (the slot permutation only
-  // depends on the lane, the rest is folded into immediate offsets).
-  int koff[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) koff[st] = l32 * RB + (((2 * st + hi) ^ k_swz<D>(l32)) << 4);
-  int voff[DB];
-  {
-    const int g = lane >> 4, i = lane & 15;
-    const int r = 4 * (g >> 1) + (i >> 2);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int c = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
-      voff[db] = r * RB + ((c ^ v_swz<D>(r)) << 4) + 8 * (i & 1);
-    }
-  }
-
-  // Copy tile j of K or V into an LDS buffer (rows at or past key_len read as
-  // zeros, with no memory traffic).
-  auto copy_tile = [&](const T* xh, int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
-    const auto rs = tile_rsrc(xh, j, BC, rr.kl, RB);
-#pragma unroll
-    for (int c = 0; c < NDMA; ++c) {
-      const int blk = c * NW + wave;
-      const int slot = blk * 64 + lane;
-      const int r = slot / CPR, ps = slot % CPR;
-      const int lc = ps ^ (decltype(is_v)::value ? v_swz<D>(r) : k_swz<D>(r));
-      lds_copy16(rs, dst + blk * 1024, r * RB + (lc << 4));
-    }
-  };
-
-  auto scores = [&](const unsigned char* kb, f32x16 (&s)[SB]) {
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      s[sb] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const v8 a = *(const v8*)(kb + 32 * sb * RB + koff[st]);
-        s[sb] = E::mma(a, qf[st], s[sb]);
-      }
-    }
-  };
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.0f;
-  const float thr = fminf(kRescaleLog2 / p.c, 1e30f);
-
-  // One pipelined iteration: softmax of tile j (scores in sc), scores of
-  // tile j+1 (into sn) and O += P_j V_j.
-  auto body = [&](int j, f32x16 (&sc)[SB], f32x16 (&sn)[SB], const unsigned char* kn,
-                  const unsigned char* vc, auto masked) {
-    if constexpr (decltype(masked)::value) apply_mask<SB, CAUSAL>(sc, j * BC, rr.kl, rr.qrow, hi);
-    float mx = sc[0][0];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[sb][i]);
-    mx = max_halves(mx);
-    const bool move = mx > m + thr;
-#if FA_RESCALE_ALWAYS
-    {
-#else
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-#endif
-      const float alpha = move ? fast_exp2((m - mx) * p.c) : 1.0f;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m = move ? mx : m;
-    }
-    scores(kn, sn);
-    const float base = (m == -INFINITY) ? 0.0f : -m * p.c;
-    v8 pf[PS];
-    float rs = 0.0f;
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[ps][e] = E::cvt(fast_exp2(fmaf(sc[ps >> 1][(ps & 1) * 8 + e], p.c, base)));
-      rs = E::sum8(pf[ps], rs);
-    }
-    l += rs;
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const unsigned char* b = vc + 16 * ps * RB + voff[db];
-        const v4 a0 = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)b));
-        const v4 a1 =
-            __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
-        o[db] = E::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), pf[ps], o[db]);
-      }
-    }
-    interleave<SB * KS, PS * DB>();
-  };
-
-  auto step = [&](int j, f32x16 (&sc)[SB], f32x16 (&sn)[SB], unsigned char* kc,
-                  unsigned char* kn, unsigned char* vc, unsigned char* vn) {
-    copy_tile(Kh, j + 2, kc, std::false_type{});  // K_j's buffer is free: S_j is done
-    copy_tile(Vh, j + 1, vn, std::true_type{});   // V_{j-1}'s buffer is free
-    if (j < rr.wfull) body(j, sc, sn, kn, vc, std::false_type{});
-    else if (j < rr.wnt) body(j, sc, sn, kn, vc, std::true_type{});
-    wait_vmem();
-    __syncthreads();
-  };
-
-  f32x16 sa[SB], sb_[SB];
-  copy_tile(Kh, 0, k0s, std::false_type{});
-  copy_tile(Kh, 1, k1s, std::false_type{});
-  copy_tile(Vh, 0, v0s, std::true_type{});
-  wait_vmem();
-  __syncthreads();
-  if (rr.wnt > 0) scores(k0s, sa);
-  __syncthreads();
-  for (int j = 0; j < rr.nt; j += 2) {
-    step(j, sa, sb_, k0s, k1s, v0s, v1s);
-    if (j + 1 < rr.nt) step(j + 1, sb_, sa, k1s, k0s, v1s, v0s);
-  }
-  epilogue<T, D, DB>(p, rr, hi, m, l, o);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 / fp16 ping-pong kernel (the default for 16-bit inputs)
-//
-// Eight waves per workgroup, 32 query rows each, in two groups of four: SIMD s
-// runs wave s of group A and wave s+4 of group B. The work of a key tile is
-// split into a matrix phase (O += P_{j-1} V_{j-1} and S_j = K_j Q^T: all the
-// MFMAs and their LDS operand reads) and a softmax phase (mask, running
-// maximum, exp2, row sums: VALU only). The two groups run the phases offset by
-// one, separated by workgroup barriers, so on every SIMD one wave keeps the
-// matrix core busy while the other does the softmax arithmetic.
-//
-//   phase 2j  :  A: matrix(j)      B: softmax(j-1)
-//   phase 2j+1:  A: softmax(j)     B: matrix(j)
-//
-// K_j and V_{j-1} are resident in LDS during phases 2j and 2j+1; the
-// direct-to-LDS copies of K_{j+1} and V_j are issued at the start of phase 2j
-// into the buffers freed by the previous pair of phases and waited for at the
-// end of phase 2j+1.
-// ---------------------------------------------------------------------------
-template <class E, int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void attn_fwd_16bit_pp(Params p) {
-  using T = typename E::T;
-  using v8 = typename E::v8;
-  using v4 = typename E::v4;
-  constexpr int NW = 8;
-  constexpr int BR = NW * 32;
-  constexpr int KS = D / 16;
-  constexpr int SB = BC / 32;
-  constexpr int DB = D / 32;
-  constexpr int PS = BC / 16;
-  constexpr int RB = D * 2;
-  constexpr int CPR = D / 8;
-  constexpr int TB = BC * RB;
-  constexpr int NCW = NW / 2;             // copying waves (group A)
-  constexpr int NDMA = TB / (1024 * NCW);  // 1 KB direct-to-LDS copies per copying wave
-  static_assert(TB % (1024 * NCW) == 0, "tile must split into 1 KB copies per wave");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool group_a = wave < 4;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
-  const int N = p.N;
-  const size_t head = (size_t)rr.bh * N * D;
-  const T* Kh = (const T*)p.k + head;
-  const T* Vh = (const T*)p.v + head;
-
-  v8 qf[KS];
-  {
-    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, RB);
-    const int off = ((rr.qrow - rr.q_wg0) * D + 8 * hi) * 2;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
-  }
-  int koff[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) koff[st] = l32 * RB + (((2 * st + hi) ^ k_swz<D>(l32)) << 4);
-  int voff[DB];
-  {
-    const int g = lane >> 4, i = lane & 15;
-    const int r = 4 * (g >> 1) + (i >> 2);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int c = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
-      voff[db] = r * RB + ((c ^ v_swz<D>(r)) << 4) + 8 * (i & 1);
-    }
-  }
-
-  auto copy_tile = [&](const T* xh, int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
-    const auto rs = tile_rsrc(xh, j, BC, rr.kl, RB);
-#pragma unroll
-    for (int c = 0; c < NDMA; ++c) {
-      const int blk = c * NCW + wave;
-      const int slot = blk * 64 + lane;
-      const int r = slot / CPR, ps = slot % CPR;
-      const int lc = ps ^ (decltype(is_v)::value ? v_swz<D>(r) : k_swz<D>(r));
-      lds_copy16(rs, dst + blk * 1024, r * RB + (lc << 4));
-    }
-  };
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  f32x16 s[SB];
-  v8 pf[PS];
-  float m = -INFINITY, l = 0.0f;
-  const float thr = fminf(kRescaleLog2 / p.c, 1e30f);
-
-  // Matrix phase of tile j: O += P_{j-1} V_{j-1} (PV steps) and S_j = K_j Q^T
-  // (S steps), one MFMA per step. The LDS operand reads run LA steps ahead of
-  // their MFMA through a small ring of registers, and the schedule barriers
-  // pin that order so the reads neither stall each MFMA nor pile up in
-  // registers. P is zero before the first tile and after the wave's last one,
-  // so the PV steps are always safe to run.
-  constexpr int NPV = PS * DB, NS = SB * KS, NSTEP = NPV + NS, LA = FA_LOOKAHEAD;
-  auto matrix = [&](const unsigned char* kb, const unsigned char* vb) __attribute__((always_inline)) {
-    v8 ring[LA + 1];
-    auto fetch = [&](int t) __attribute__((always_inline)) {
-      if (t < NPV) {
-        const unsigned char* b = vb + 16 * (t / DB) * RB + voff[t % DB];
-        const v4 a0 = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)b));
-        const v4 a1 = __builtin_bit_cast(
-            v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
-        ring[t % (LA + 1)] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-      } else {
-        const int u = t - NPV;
-        ring[t % (LA + 1)] = *(const v8*)(kb + 32 * (u / KS) * RB + koff[u % KS]);
-      }
-    };
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < NSTEP + LA; ++t) {
-      if (t < NSTEP) fetch(t);
-      const int u = t - LA;
-      if (u >= 0) {
-        if (u < NPV) o[u % DB] = E::mma(ring[u % (LA + 1)], pf[u / DB], o[u % DB]);
-        else s[(u - NPV) / KS] = E::mma(ring[u % (LA + 1)], qf[(u - NPV) % KS], s[(u - NPV) / KS]);
-      }
-    }
-#if FA_SCHED
-#pragma unroll
-    for (int t = 0; t < NSTEP + LA; ++t) {
-      if (t < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else if (t < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (t >= LA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-#endif
-  };
-
-  // Softmax phase of tile j: scores in s -> P_j in pf, running max / sum.
-  auto softmax = [&](int j, auto masked) __attribute__((always_inline)) {
-    if constexpr (decltype(masked)::value) apply_mask<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi);
-    float mx = s[0][0];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-    mx = max_halves(mx);
-    const bool move = mx > m + thr;
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-      const float alpha = move ? fast_exp2((m - mx) * p.c) : 1.0f;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m = move ? mx : m;
-    }
-    const float base = (m == -INFINITY) ? 0.0f : -m * p.c;
-    float rs = 0.0f;
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[ps][e] = E::cvt(fast_exp2(fmaf(s[ps >> 1][(ps & 1) * 8 + e], p.c, base)));
-      rs = E::sum8(pf[ps], rs);
-    }
-    l += rs;
-  };
-  auto clear_p = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps) pf[ps] = v8{};
-  };
-
-  // Group B runs one phase behind group A: it passes one extra barrier first
-  // and skips the very last one, so both groups execute the same code path.
-  // Group A issues every K/V copy (so the copies' wait always closes the
-  // phase pair they must land in).
-  const int nt = rr.nt;
-  clear_p();
-  copy_tile(Kh, 0, k0s, std::false_type{});
-  if (group_a) wait_vmem();
-  __syncthreads();
-  if (!group_a) __syncthreads();
-  auto trip = [&](int j, unsigned char* kc, unsigned char* kn, unsigned char* vc,
-                  unsigned char* vp) __attribute__((always_inline)) {
-    if (group_a) {
-      if (j + 1 < nt) copy_tile(Kh, j + 1, kn, std::false_type{});
-      if (j < nt) copy_tile(Vh, j, vc, std::true_type{});
-    }
-    if (j - 1 < rr.wnt) matrix(kc, vp);  // PV_{j-1} and S_j
-    __syncthreads();
-    if (j < rr.wfull) softmax(j, std::false_type{});
-    else if (j < rr.wnt) softmax(j, std::true_type{});
-    else clear_p();
-    if (group_a) wait_vmem();
-    if (group_a || j < nt) __syncthreads();
-  };
-  for (int j = 0; j <= nt; j += 2) {
-    trip(j, k0s, k1s, v0s, v1s);
-    if (j + 1 <= nt) trip(j + 1, k1s, k0s, v1s, v0s);
-  }
-  epilogue<T, D, DB>(p, rr, hi, m, l, o);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 / fp16 kernel with two row groups per wave (the default for 16-bit)
-//
-// Four waves per workgroup, one per SIMD, each owning 64 query rows as two
-// 32-row MFMA groups (A and B). Every K or V operand read from LDS feeds one
-// MFMA of each group, which halves LDS operand traffic per MFMA compared with
-// one group per wave -- the operand reads, not the matrix cores or the
-// softmax arithmetic, are what bounds the one-group kernel.
-//
-// Within an iteration the wave's own instruction stream overlaps the two
-// halves of the work: after S_j = K_j Q^T (both groups), the online softmax
-// of tile j runs on the VALU while the matrix cores do O += P_{j-1} V_{j-1}
-// for the previous tile. A rare rescale of O (when a row's reference maximum
-// moves) is applied after that product and before the next one. LDS holds
-// K_j and V_{j-1} during iteration j while the direct-to-LDS copies of
-// K_{j+1} and V_j land in the other two buffers; one barrier per iteration.
-// ---------------------------------------------------------------------------
-template <class E, int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_fwd_16bit_2g(Params p) {
-  using T = typename E::T;
-  using v8 = typename E::v8;
-  using v4 = typename E::v4;
-  constexpr int NW = 4;
-  constexpr int BR = NW * 64;
+  static_assert(NBUF == 2 || NBUF == 3, "two or three LDS buffers per operand");
   constexpr int KS = D / 16;
   constexpr int SB = BC / 32;
   constexpr int DB = D / 32;
@@ -917,58 +532,36 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_16bit_2g(Params p) {
   constexpr int CPR = D / 8;
   constexpr int TB = BC * RB;
   constexpr int NDMA = TB / (1024 * NW);
+  constexpr int NS = SB * KS, NPV = PS * DB;
+  constexpr int LA = FA_LOOKAHEAD;
   static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB copies per wave");
 
+  // One named array per buffer (not one 2-D array): distinct objects let the
+  // compiler see that an in-flight copy into one buffer cannot alias operand
+  // reads from another, so it does not wait for the copy before them.
+  constexpr int TB3 = NBUF == 3 ? TB : 16;
   __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k2s[TB3];
   __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v2s[TB3];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
+  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
-
-  // Tile ranges. nt: key tiles the workgroup streams; wfull: tiles that need
-  // no mask for any row of this wave. Tiles past a wave's diagonal are still
-  // multiplied (their keys are all masked, so they add nothing): one wave per
-  // SIMD waits at the barrier for the slowest wave anyway.
-  RowRange ra;
-  int qt;
-  map_block(p.n_qt, CAUSAL, ra.bh, qt);
-  ra.b = ra.bh / p.H;
-  int kl = N;
-  if (p.key_len != nullptr) {
-    const int x = p.key_len[ra.b];
-    kl = x < 0 ? 0 : (x > N ? N : x);
-  }
-  kl = __builtin_amdgcn_readfirstlane(kl);
-  ra.kl = kl;
-  ra.q_wg0 = qt * BR;
-  ra.qw0 = ra.q_wg0 + wave * 64;
-  ra.qrow = ra.qw0 + l32;
-  RowRange rb = ra;
-  rb.qrow = ra.qrow + 32;
-  int kv_end = kl;
-  if (CAUSAL) kv_end = min(kv_end, min(N, ra.q_wg0 + BR));
-  const int nt = (kv_end + BC - 1) / BC;
-  int full = kl / BC;
-  if (CAUSAL) full = min(full, (ra.qw0 + 1) / BC);
-  const int wfull = full;
-
-  const size_t head = (size_t)ra.bh * N * D;
+  const size_t head = (size_t)rr.bh * N * D;
   const T* Kh = (const T*)p.k + head;
   const T* Vh = (const T*)p.v + head;
 
-  v8 qa[KS], qb[KS];
+  v8 qf[KS];
   {
-    const auto rq = tile_rsrc((const T*)p.q + head, qt, BR, N, RB);
-    const int off = ((ra.qrow - ra.q_wg0) * D + 8 * hi) * 2;
+    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, RB);
+    const int off = ((rr.qrow - rr.q_wg0) * D + 8 * hi) * 2;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qa[s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
-      qb[s] = __builtin_bit_cast(v8, load16(rq, off + 32 * RB + 32 * s));
-    }
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
   }
   int koff[KS];
 #pragma unroll
@@ -985,7 +578,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_16bit_2g(Params p) {
   }
 
   auto copy_tile = [&](const T* xh, int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
-    const auto rs = tile_rsrc(xh, j, BC, kl, RB);
+    const auto rs = tile_rsrc(xh, j, BC, rr.kl, RB);
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       const int blk = c * NW + wave;
@@ -995,115 +588,88 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_16bit_2g(Params p) {
       lds_copy16(rs, dst + blk * 1024, r * RB + (lc << 4));
     }
   };
+  auto kfrag = [&](const unsigned char* kb, int u) __attribute__((always_inline)) {
+    return *(const v8*)(kb + 32 * (u / KS) * RB + koff[u % KS]);  // u = sb*KS + st
+  };
+  auto vfrag = [&](const unsigned char* vb, int u) __attribute__((always_inline)) {
+    const unsigned char* b = vb + 16 * (u / DB) * RB + voff[u % DB];  // u = ps*DB + db
+    const v4 a0 = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)b));
+    const v4 a1 =
+        __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
+    return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
-  f32x16 oa[DB], ob[DB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oa[db] = ob[db] = f32x16{};
-  f32x16 sa[SB], sb[SB];
-  v8 pa[PS], pb[PS];
-  float ma = -INFINITY, la = 0.0f, mb = -INFINITY, lb = 0.0f;
-  float alpha_a = 1.0f, alpha_b = 1.0f;
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
   const float thr = fminf(kRescaleLog2 / p.c, 1e30f);
 
-  // S_j = K_j Q^T for both groups: each K fragment feeds two MFMAs.
-  auto scores = [&](const unsigned char* kb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int x = 0; x < SB; ++x) sa[x] = sb[x] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-#pragma unroll
-      for (int x = 0; x < SB; ++x) {
-        const v8 a = *(const v8*)(kb + 32 * x * RB + koff[st]);
-        sa[x] = E::mma(a, qa[st], sa[x]);
-        sb[x] = E::mma(a, qb[st], sb[x]);
-      }
-  };
-  // O += P V for both groups: each V fragment feeds two MFMAs.
-  auto pv = [&](const unsigned char* vb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const unsigned char* b = vb + 16 * ps * RB + voff[db];
-        const v4 a0 = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)b));
-        const v4 a1 = __builtin_bit_cast(
-            v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
-        const v8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oa[db] = E::mma(a, pa[ps], oa[db]);
-        ob[db] = E::mma(a, pb[ps], ob[db]);
-      }
-  };
-  // Online softmax of one group's scores; returns whether the reference moved.
-  auto softmax = [&](f32x16 (&s)[SB], v8 (&pf)[PS], float& m, float& l, float& alpha)
+  auto tile = [&](int j, const unsigned char* kb, const unsigned char* vb, auto masked)
       __attribute__((always_inline)) {
-    float mx = s[0][0];
+    // S = K Q^T, operand reads LA steps ahead
+    f32x16 s[SB];
 #pragma unroll
-    for (int x = 0; x < SB; ++x)
+    for (int x = 0; x < SB; ++x) s[x] = f32x16{};
+    v8 ring[LA + 1];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[x][i]);
-    mx = max_halves(mx);
-    const bool move = mx > m + thr;  // true on the first live tile (m = -inf)
-    alpha = move ? fast_exp2((m - mx) * p.c) : 1.0f;  // exp2(-inf) = 0
-    m = move ? mx : m;
-    const float base = (m == -INFINITY) ? 0.0f : -m * p.c;
-    float rs = 0.0f;
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[ps][e] = E::cvt(fast_exp2(fmaf(s[ps >> 1][(ps & 1) * 8 + e], p.c, base)));
-      rs = E::sum8(pf[ps], rs);
+    for (int t = 0; t < NS + LA; ++t) {
+      if (t < NS) ring[t % (LA + 1)] = kfrag(kb, t);
+      const int u = t - LA;
+      if (u >= 0) s[u / KS] = E::mma(ring[u % (LA + 1)], qf[u % KS], s[u / KS]);
     }
-    l = alpha * l + rs;
-    return move;
-  };
-  auto rescale = [&]() __attribute__((always_inline)) {
-    // an empty asm statement with side effects keeps the compiler from
-    // hoisting this rarely taken block into the main path
-    __asm__ volatile("" ::: "memory");
+    // first V operands, in flight during the softmax
+    v8 vring[LA + 1];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int t = 0; t < LA; ++t) vring[t] = vfrag(vb, t);
+    if constexpr (decltype(masked)::value) apply_mask<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi);
+    v8 pf[PS];
+    online_softmax<E, SB, DB>(s, p.c, thr, m, l, o, pf);
+    // O += P V, operand reads LA steps ahead
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        oa[db][i] *= alpha_a;
-        ob[db][i] *= alpha_b;
-      }
-  };
-  // Iteration j. K_j is in kc, V_{j-1} in vp; K_{j+1} goes to kn, V_j to vc.
-  auto iter = [&](int j, const unsigned char* kc, unsigned char* kn, unsigned char* vc,
-                  const unsigned char* vp, auto first) __attribute__((always_inline)) {
-    if (j + 1 < nt) copy_tile(Kh, j + 1, kn, std::false_type{});
-    copy_tile(Vh, j, vc, std::true_type{});
-    scores(kc);
-    if (j >= wfull) {
-      apply_mask<SB, CAUSAL>(sa, j * BC, kl, ra.qrow, hi);
-      apply_mask<SB, CAUSAL>(sb, j * BC, kl, rb.qrow, hi);
+    for (int t = LA; t < NPV + LA; ++t) {
+      if (t < NPV) vring[t % (LA + 1)] = vfrag(vb, t);
+      const int u = t - LA;
+      o[u % DB] = E::mma(vring[u % (LA + 1)], pf[u / DB], o[u % DB]);
     }
-    if constexpr (!decltype(first)::value) pv(vp);  // P_{j-1} V_{j-1}, overlapping the softmax
-    const bool mva = softmax(sa, pa, ma, la, alpha_a);
-    const bool mvb = softmax(sb, pb, mb, lb, alpha_b);
-    if (__builtin_amdgcn_ballot_w64(mva || mvb) != 0) rescale();
-    wait_vmem();
+  };
+  // Iteration j uses buffer j % NBUF and copies tile j + NBUF - 1 into the
+  // buffer iteration j - 1 used. Copies are issued even for tiles past the end
+  // (their byte range is empty, so they move nothing) to keep the counts below
+  // exact: at the end of iteration j only the copies issued in it may remain
+  // in flight when NBUF == 3.
+  constexpr int KEEP = (NBUF - 2) * 2 * NDMA;  // copies one iteration may leave in flight
+  auto step = [&](int j, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
+                  unsigned char* vn) __attribute__((always_inline)) {
+    copy_tile(Kh, j + NBUF - 1, kn, std::false_type{});
+    copy_tile(Vh, j + NBUF - 1, vn, std::true_type{});
+    if (j < rr.wfull) tile(j, kc, vc, std::false_type{});
+    else if (j < rr.wnt) tile(j, kc, vc, std::true_type{});
+    wait_vmem_keep<KEEP>();
     __syncthreads();
   };
 
   copy_tile(Kh, 0, k0s, std::false_type{});
-  wait_vmem();
-  __syncthreads();
-  if (nt > 0) {
-    iter(0, k0s, k1s, v0s, v1s, std::true_type{});
-    int j = 1;
-    for (; j + 1 < nt; j += 2) {
-      iter(j, k1s, k0s, v1s, v0s, std::false_type{});
-      iter(j + 1, k0s, k1s, v0s, v1s, std::false_type{});
-    }
-    if (j < nt) iter(j, k1s, k0s, v1s, v0s, std::false_type{});
-    // the last tile's P V (its V landed during the last iteration)
-    if ((nt - 1) & 1) pv(v1s);
-    else pv(v0s);
+  copy_tile(Vh, 0, v0s, std::true_type{});
+  if constexpr (NBUF == 3) {
+    copy_tile(Kh, 1, k1s, std::false_type{});
+    copy_tile(Vh, 1, v1s, std::true_type{});
   }
-  epilogue<T, D, DB>(p, ra, hi, ma, la, oa);
-  epilogue<T, D, DB>(p, rb, hi, mb, lb, ob);
+  wait_vmem_keep<KEEP>();
+  __syncthreads();
+  if constexpr (NBUF == 2) {
+    for (int j = 0; j < rr.nt; j += 2) {
+      step(j, k0s, v0s, k1s, v1s);
+      if (j + 1 < rr.nt) step(j + 1, k1s, v1s, k0s, v0s);
+    }
+  } else {
+    for (int j = 0; j < rr.nt; j += 3) {
+      step(j, k0s, v0s, k2s, v2s);
+      if (j + 1 < rr.nt) step(j + 1, k1s, v1s, k0s, v0s);
+      if (j + 2 < rr.nt) step(j + 2, k2s, v2s, k1s, v1s);
+    }
+  }
+  epilogue<T, D, DB>(p, rr, hi, m, l, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -1335,7 +901,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
       mx = max_halves(mx);
       const float m_new = fmaxf(m, mx);
       if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-        const float alpha = (m_new > m) ? fast_exp2((m - m_new) * p.c) : 1.0f;
+        const float alpha = pinned((m_new > m) ? fast_exp2((m - m_new) * p.c) : 1.0f);
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -1390,15 +956,13 @@ template <int D, bool C>
 hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
   constexpr int T = kWaves * 64;
   switch (kind) {
-#if FA_PIPE == 3
-    case Kind::BF16: return launch(attn_fwd_16bit_2g<Bf16, D, FA_KEY_TILE, C>, p, 256, s);
-    case Kind::F16: return launch(attn_fwd_16bit_2g<F16, D, FA_KEY_TILE, C>, p, 256, s);
-#elif FA_PIPE == 2
-    case Kind::BF16: return launch(attn_fwd_16bit_pp<Bf16, D, FA_KEY_TILE, C>, p, 512, s);
-    case Kind::F16: return launch(attn_fwd_16bit_pp<F16, D, FA_KEY_TILE, C>, p, 512, s);
-#elif FA_PIPE == 1
-    case Kind::BF16: return launch(attn_fwd_16bit_pipe<Bf16, D, kWaves, FA_KEY_TILE, C>, p, T, s);
-    case Kind::F16: return launch(attn_fwd_16bit_pipe<F16, D, kWaves, FA_KEY_TILE, C>, p, T, s);
+#if FA_16BIT_KERNEL == 1
+    case Kind::BF16:
+      return launch(attn_fwd_16bit_dma<Bf16, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C>, p,
+                    FA_DMA_WAVES * 64, s);
+    case Kind::F16:
+      return launch(attn_fwd_16bit_dma<F16, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C>, p,
+                    FA_DMA_WAVES * 64, s);
 #else
     case Kind::BF16: return launch(attn_fwd_16bit<Bf16, D, kWaves, FA_KEY_TILE, C>, p, T, s);
     case Kind::F16: return launch(attn_fwd_16bit<F16, D, kWaves, FA_KEY_TILE, C>, p, T, s);
@@ -1413,8 +977,8 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
 
 int rows_per_block(Kind kind, int d) {
   if (d != 64 && d != 128) return 0;
-#if FA_PIPE == 2 || FA_PIPE == 3
-  if (kind == Kind::BF16 || kind == Kind::F16) return 256;
+#if FA_16BIT_KERNEL == 1
+  if (kind == Kind::BF16 || kind == Kind::F16) return FA_DMA_WAVES * 32;
 #endif
   return kWaves * 32;
 }
