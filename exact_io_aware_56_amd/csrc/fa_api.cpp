@@ -45,7 +45,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
 
   const fa::Kind kind = static_cast<fa::Kind>(dtype);
-  const int rows = fa::rows_per_block(kind, d);
+  const int rows = fa::rows_per_block(kind, d, N, causal != 0);
   fa::Params p;
   p.q = Q;
   p.k = K;

@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "fa_internal.h"
 
@@ -76,10 +77,30 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #define FA_WAVES_PER_EU 2
 #endif
 #ifndef FA_16BIT_KERNEL
-#define FA_16BIT_KERNEL 1  // 16-bit inputs: 0 register-staged kernel, 1 direct-to-LDS kernel
+// 16-bit inputs: 0 register-staged kernel, 1 direct-to-LDS kernel, 2 pipelined
+// kernel, 3 pipelined kernel for N >= FA_PIPE_MIN_N and direct-to-LDS below
+#define FA_16BIT_KERNEL 3
+#endif
+#ifndef FA_PIPE_MIN_N
+#define FA_PIPE_MIN_N 4096
 #endif
 #ifndef FA_DMA_WAVES
 #define FA_DMA_WAVES 4  // waves per workgroup of the direct-to-LDS kernel
+#endif
+#ifndef FA_WIDE_WAVES
+#define FA_WIDE_WAVES 8  // waves per workgroup of the pipelined kernel
+#endif
+#ifndef FA_PIPE_NBUF
+#define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
+#endif
+#ifndef FA_PIPE_SCHED
+#define FA_PIPE_SCHED 0  // VALU instructions placed after each MFMA of a pipeline step (0: compiler's order)
+#endif
+#ifndef FA_PIPE_SCHED_DS
+#define FA_PIPE_SCHED_DS 2  // LDS reads placed after each MFMA when FA_PIPE_SCHED is set
+#endif
+#ifndef FA_WIDE_GROUPS
+#define FA_WIDE_GROUPS 1  // 32-row groups per wave of the pipelined kernel (1 or 2)
 #endif
 #ifndef FA_NBUF
 #define FA_NBUF 2  // LDS buffers per operand in the direct-to-LDS kernel (2 or 3)
@@ -112,6 +133,10 @@ __device__ __forceinline__ float pinned(float x) {
   __asm__ volatile("" : "+v"(x));
   return x;
 }
+__device__ __forceinline__ int pinned_int(int x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
 
 // Raw buffer resource (gfx9 descriptor word 3) over `bytes` bytes at `base`.
 // Loads at offsets >= bytes return zeros without touching memory, which is how
@@ -141,17 +166,28 @@ __device__ __forceinline__ i32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
 }
 
 // Workgroup -> (batch*head, query tile). Workgroups are handed to the XCDs
-// round-robin by id, so id % 8 names the XCD. Each XCD receives a contiguous
-// run of logical tiles (whole heads when B*H is a multiple of 8) so the
-// workgroups that run together on one XCD read the same head's K/V through
-// that XCD's L2. Causal tiles are issued longest-first (last query tile first)
-// so the short tiles fill the tail of the launch.
+// round-robin by id, so id % 8 names the XCD. When B*H is a multiple of 8,
+// each XCD owns B*H/8 whole heads, so the workgroups that run together on one
+// XCD read those heads' K/V through that XCD's L2, and within an XCD the
+// workgroups are issued query-tile-major over its heads: for causal attention
+// the last (longest) query tiles of every head first, the shortest last, so
+// that the short ones fill the tail of the launch whatever the run-time
+// spread of the long ones. Otherwise tiles are issued head by head, causal
+// ones longest first, in contiguous runs per XCD when the grid divides.
 __device__ __forceinline__ void map_block(int n_qt, bool causal, int& bh, int& qt) {
   const int bid = blockIdx.x, total = gridDim.x;
-  int logical = bid;
-  if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
-  bh = logical / n_qt;
-  const int r = logical - bh * n_qt;
+  int r;
+  if (total % (kXcds * n_qt) == 0) {
+    const int hx = total / (kXcds * n_qt);  // heads per XCD
+    const int i = bid / kXcds;              // issue rank within the XCD
+    bh = (bid % kXcds) * hx + i % hx;
+    r = i / hx;
+  } else {
+    int logical = bid;  // contiguous runs of tiles per XCD when possible
+    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+    bh = logical / n_qt;
+    r = logical - bh * n_qt;
+  }
   qt = causal ? (n_qt - 1 - r) : r;
 }
 
@@ -163,11 +199,11 @@ struct RowRange {
 // multiplies (wnt): keys at or beyond key_len, and for causal keys beyond the
 // last row of the workgroup / wave, can only be masked, so those tiles are
 // skipped altogether.
-template <int BR, int BC, bool CAUSAL>
-__device__ __forceinline__ RowRange row_range(const Params& p, int wave, int l32) {
+template <int BR, int BC, bool CAUSAL, int WR = 32>
+__device__ __forceinline__ RowRange row_range_at(const Params& p, int bh, int qt, int wave,
+                                                 int l32) {
   RowRange r;
-  int qt;
-  map_block(p.n_qt, CAUSAL, r.bh, qt);
+  r.bh = bh;
   r.b = r.bh / p.H;
   const int N = p.N;
   int kl = N;
@@ -180,13 +216,13 @@ __device__ __forceinline__ RowRange row_range(const Params& p, int wave, int l32
   // sides executed under an exec mask) instead of a scalar branch.
   r.kl = kl = __builtin_amdgcn_readfirstlane(kl);
   r.q_wg0 = qt * BR;
-  r.qw0 = r.q_wg0 + wave * 32;
+  r.qw0 = r.q_wg0 + wave * WR;
   r.qrow = r.qw0 + l32;
   int kv_end = kl;
   if (CAUSAL) kv_end = min(kv_end, min(N, r.q_wg0 + BR));
   r.nt = (kv_end + BC - 1) / BC;
   int w_end = kv_end;
-  if (CAUSAL) w_end = min(w_end, r.qw0 + 32);
+  if (CAUSAL) w_end = min(w_end, r.qw0 + WR);
   if (r.qw0 >= N) w_end = 0;
   r.wnt = (w_end + BC - 1) / BC;
   // Tiles [0, wfull) need no mask for any row of this wave: every key is below
@@ -197,6 +233,13 @@ __device__ __forceinline__ RowRange row_range(const Params& p, int wave, int l32
   return r;
 }
 
+template <int BR, int BC, bool CAUSAL, int WR = 32>
+__device__ __forceinline__ RowRange row_range(const Params& p, int wave, int l32) {
+  int bh, qt;
+  map_block(p.n_qt, CAUSAL, bh, qt);
+  return row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit element policies
 // ---------------------------------------------------------------------------
@@ -204,6 +247,9 @@ struct Bf16 {
   using T = __bf16;
   using v8 = bf16x8;
   using v4 = bf16x4;
+  // Largest P the pipelined kernel lets a stale reference maximum produce:
+  // bf16 has fp32's exponent range, and O and l accumulate in fp32.
+  static constexpr float kPBound = 0x1p64f;
   static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -225,6 +271,7 @@ struct F16 {
   using T = _Float16;
   using v8 = f16x8;
   using v4 = f16x4;
+  static constexpr float kPBound = 0x1p15f;  // below fp16's largest finite value
   static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -338,14 +385,14 @@ __device__ __forceinline__ void pv_product(const typename E::T* vt, int lane,
 
 // Final normalisation and the single write of O (16-bit) and LSE.
 template <class OutT, int D, int DB>
-__device__ __forceinline__ void epilogue(const Params& p, const RowRange& rr, int hi, float m,
-                                         float l, const f32x16 (&o)[DB]) {
+__device__ __forceinline__ void epilogue_row(const Params& p, int bh, int qrow, int hi, float m,
+                                             float l, const f32x16 (&o)[DB]) {
   typedef OutT v4 __attribute__((ext_vector_type(4)));
   const float lt = sum_halves(l);
   const bool live = lt > 0.0f;
   const float inv = live ? p.o_scale / lt : 0.0f;
-  if (rr.qrow < p.N) {
-    OutT* orow = (OutT*)p.o + ((size_t)rr.bh * p.N + rr.qrow) * D;
+  if (qrow < p.N) {
+    OutT* orow = (OutT*)p.o + ((size_t)bh * p.N + qrow) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -356,8 +403,57 @@ __device__ __forceinline__ void epilogue(const Params& p, const RowRange& rr, in
         *(v4*)(orow + 32 * db + 8 * g + 4 * hi) = out;
       }
     if (hi == 0)
-      p.lse[(size_t)rr.bh * p.N + rr.qrow] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
+      p.lse[(size_t)bh * p.N + qrow] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
   }
+}
+
+template <class OutT, int D, int DB>
+__device__ __forceinline__ void epilogue(const Params& p, const RowRange& rr, int hi, float m,
+                                         float l, const f32x16 (&o)[DB]) {
+  epilogue_row<OutT, D, DB>(p, rr.bh, rr.qrow, hi, m, l, o);
+}
+
+// The same for the 32 rows [row0, row0 + 32) of one wave, with O staged
+// through `stage` (32 * D 16-bit elements of LDS owned by this wave) so that
+// each global store covers whole rows. Written straight from the accumulator
+// layout a row leaves a lane pair as 8-byte pieces, and lines that L2 evicts
+// half written cost extra memory writes.
+template <class OutT, int D, int DB>
+__device__ __forceinline__ void epilogue_staged(const Params& p, int bh, int row0, int lane,
+                                                float m, float l, const f32x16 (&o)[DB],
+                                                unsigned char* stage) {
+  typedef OutT v4 __attribute__((ext_vector_type(4)));
+  constexpr int RB = D * 2, CPR = D / 8;  // bytes and 16-byte slots per row
+  // Addresses come from an opaque copy of the lane index: computed here, not
+  // hoisted to the kernel's start and kept live (or spilled) meanwhile.
+  lane = pinned_int(lane);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const float lt = sum_halves(l);
+  const bool live = lt > 0.0f;
+  const float inv = live ? p.o_scale / lt : 0.0f;
+  // Slot c of row r is stored at slot c ^ (r % CPR): the 32 rows a store
+  // instruction touches then spread over the banks.
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      v4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (OutT)(o[db][4 * g + e] * inv);
+      const int c = 4 * db + g;
+      *(FA_LDS v4*)(stage + l32 * RB + ((c ^ (l32 % CPR)) << 4) + 8 * hi) = out;
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = k * RPI + lane / CPR, c = lane % CPR;
+    const i32x4 v = *(FA_LDS const i32x4*)(stage + r * RB + ((c ^ (r % CPR)) << 4));
+    if (row0 + r < p.N) *(i32x4*)((OutT*)p.o + ((size_t)bh * p.N + row0 + r) * D + 8 * c) = v;
+  }
+  if (hi == 0 && row0 + l32 < p.N)
+    p.lse[(size_t)bh * p.N + row0 + l32] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -672,6 +768,341 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   epilogue<T, D, DB>(p, rr, hi, m, l, o);
 }
 
+// Calls f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{}).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel, software-pipelined (the default for 16-bit inputs).
+//
+// The unit of work is a 32-key half h of a 64-key LDS tile:
+//   S(h) = K(h) Q^T (MFMA),  P(h) from S(h) (vector ALU),  O += V(h)^T P(h)^T (MFMA).
+// Step h issues the MFMAs of S(h+1) and of O += V(h-1)^T P(h-1)^T while the
+// vector ALU turns S(h) into P(h). The two MFMA streams and the vector work
+// of a step do not depend on each other, so a single wave keeps the matrix
+// core and the ALU busy at the same time. K runs one tile ahead of V:
+// iteration t reads K of tile t+1 and V of tile t while the copies of K t+2
+// and V t+1 land (two LDS buffers per operand).
+//
+// The reference maximum is lazy and needs no row maximum per tile. P(h) is
+// formed against the row's current reference m; since the row sum of P(h)
+// is needed anyway, it also tells whether any score got too far above m: if
+// a lane's partial sum exceeds E::kPBound, or is inf / NaN (first tile, where
+// m = -inf), a rarely taken branch takes the true maximum of the half, moves
+// m there, rescales O and l and recomputes P(h). Otherwise every P is at most
+// E::kPBound, which the 16-bit P and the fp32 accumulators hold without loss,
+// and O / l is the same exact softmax for any reference.
+//
+// With G = 2 a wave owns 64 query rows as two 32-row groups sharing every K
+// and V operand read; G = 1 keeps 32 rows per wave and two waves per SIMD.
+// Within a wave at most one key tile needs a mask (a tile covers a wave's row
+// range, see row_range), and it is the wave's last tile.
+// ---------------------------------------------------------------------------
+
+template <class E, int D, int G, int NW, int NB, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  using v4 = typename E::v4;
+  static_assert(G == 1 || G == 2, "one or two 32-row groups per wave");
+  constexpr int WR = 32 * G;   // query rows per wave
+  constexpr int BR = NW * WR;  // query rows per workgroup
+  constexpr int BC = 64;       // keys per LDS tile
+  constexpr int KS = D / 16;   // MFMA steps over the head dim
+  constexpr int DB = D / 32;   // 32-wide head-dim blocks of O^T
+  constexpr int RB = D * 2;    // bytes per K / V row
+  constexpr int CPR = D / 8;   // 16-byte slots per row
+  constexpr int TB = BC * RB;  // bytes per tile
+  constexpr int NDMA = TB / (1024 * NW);
+  constexpr int NPV = 2 * DB;  // PV MFMA steps per half (2 x 16 keys)
+  constexpr int LA = FA_LOOKAHEAD;
+  static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB copies per wave");
+  static_assert(NB >= 2 && NB <= 4, "two to four LDS buffers per operand");
+
+  // One named array per buffer: distinct objects let the compiler see that a
+  // copy in flight into one buffer cannot alias operand reads from another.
+  constexpr int TB2 = NB > 2 ? TB : 16, TB3 = NB > 3 ? TB : 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k2s[TB2];
+  __shared__ __attribute__((aligned(1024))) unsigned char k3s[TB3];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v2s[TB2];
+  __shared__ __attribute__((aligned(1024))) unsigned char v3s[TB3];
+  auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? k0s : i == 1 ? k1s : i == 2 ? k2s : k3s;
+  };
+  auto vbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? v0s : i == 1 ? v1s : i == 2 ? v2s : v3s;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int N = p.N;
+
+  // One query tile of one head, start to finish.
+  auto process = [&](int bh, int qt) __attribute__((always_inline)) {
+  // Lane-derived offsets are recomputed per tile from an opaque copy of the
+  // lane index, so that they are not kept live (and spilled) across tiles.
+  const int ln = pinned_int(lane);
+  int koff[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    koff[st] = (ln & 31) * RB + (((2 * st + (ln >> 5)) ^ k_swz<D>(ln & 31)) << 4);
+  int voff[DB];
+  {
+    const int g = ln >> 4, i = ln & 15;
+    const int r = 4 * (g >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
+      voff[db] = r * RB + ((c ^ v_swz<D>(r)) << 4) + 8 * (i & 1);
+    }
+  }
+  const RowRange rr = row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
+  const size_t head = (size_t)rr.bh * N * D;
+  const T* Kh = (const T*)p.k + head;
+  const T* Vh = (const T*)p.v + head;
+
+  v8 qf[G][KS];
+  {
+    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, RB);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int off = ((rr.qrow + 32 * g - rr.q_wg0) * D + 8 * hi) * 2;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[g][s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
+    }
+  }
+  auto copy_tile = [&](const T* xh, int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
+    const auto rs = tile_rsrc(xh, j, BC, rr.kl, RB);
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) {
+      const int blk = c * NW + wave;
+      const int slot = blk * 64 + lane;
+      const int r = slot / CPR, ps = slot % CPR;
+      const int lc = ps ^ (decltype(is_v)::value ? v_swz<D>(r) : k_swz<D>(r));
+      lds_copy16(rs, dst + blk * 1024, r * RB + (lc << 4));
+    }
+  };
+  // K operand of MFMA step st over keys [32*h, 32*h + 32) of the tile at kb
+  auto kfrag = [&](const unsigned char* kb, int h, int st) __attribute__((always_inline)) {
+    return *(const v8*)(kb + 32 * h * RB + koff[st]);
+  };
+  // V^T operand of PV step u = ps*DB + db over keys 32*h + 16*ps + [0, 16)
+  auto vfrag = [&](const unsigned char* vb, int h, int u) __attribute__((always_inline)) {
+    const unsigned char* b = vb + (32 * h + 16 * (u / DB)) * RB + voff[u % DB];
+    const v4 a0 = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)b));
+    const v4 a1 =
+        __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
+    return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // S^T = K Q^T over one 32-key half for every group, each K operand read once
+  auto scores = [&](const unsigned char* kb, int h, f32x16 (&s)[G]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = f32x16{};
+    v8 ring[LA + 1];
+#pragma unroll
+    for (int t = 0; t < KS + LA; ++t) {
+      if (t < KS) ring[t % (LA + 1)] = kfrag(kb, h, t);
+      const int u = t - LA;
+      if (u >= 0)
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[g] = E::mma(ring[u % (LA + 1)], qf[g][u], s[g]);
+    }
+  };
+
+  f32x16 o[G][DB];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[g][db] = f32x16{};
+  // m: reference maximum (raw score units); base = -m * c, +inf while m = -inf
+  float m[G], base[G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) m[g] = -INFINITY, base[g] = INFINITY, l[g] = 0.0f;
+  const float c = p.c;
+
+  // O += V^T P^T over one 32-key half, each V operand read once
+  auto pv = [&](const unsigned char* vb, int h, const v8 (&pf)[G][2]) __attribute__((always_inline)) {
+    v8 ring[LA + 1];
+#pragma unroll
+    for (int t = 0; t < NPV + LA; ++t) {
+      if (t < NPV) ring[t % (LA + 1)] = vfrag(vb, h, t);
+      const int u = t - LA;
+      if (u >= 0)
+#pragma unroll
+        for (int g = 0; g < G; ++g) o[g][u % DB] = E::mma(ring[u % (LA + 1)], pf[g][u / DB], o[g][u % DB]);
+    }
+  };
+  // P of one half from its raw scores s (k0 = its first key); updates l and,
+  // on the rare branch, m, base and O.
+  auto probs = [&](f32x16 (&s)[G], v8 (&pf)[G][2], int k0, auto masked) __attribute__((always_inline)) {
+    float rs[G];
+    bool bad = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if constexpr (decltype(masked)::value)
+        apply_mask<1, CAUSAL>(*reinterpret_cast<f32x16(*)[1]>(&s[g]), k0, rr.kl, rr.qrow + 32 * g, hi);
+      rs[g] = 0.0f;
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[g][ps][e] = E::cvt(fast_exp2(fmaf(s[g][8 * ps + e], c, base[g])));
+        rs[g] = E::sum8(pf[g][ps], rs[g]);
+      }
+      bad |= !(rs[g] <= E::kPBound);
+    }
+#if FA_PIPE_SCHED
+    // Spread the step's vector work and LDS reads evenly between its MFMAs.
+    static_for<2 * KS * G>([&](auto) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, FA_PIPE_SCHED_DS, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, FA_PIPE_SCHED, 0);  // VALU
+    });
+#endif
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float x = s[g][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, s[g][i]);
+        const float mn = fmaxf(m[g], max_halves(x));
+        const float alpha = pinned(mn == m[g] ? 1.0f : fast_exp2((m[g] - mn) * c));
+        l[g] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha;
+        m[g] = mn;
+        base[g] = -mn * c;
+        const float bu = mn == -INFINITY ? 0.0f : base[g];
+        rs[g] = 0.0f;
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[g][ps][e] = E::cvt(fast_exp2(fmaf(s[g][8 * ps + e], c, bu)));
+          rs[g] = E::sum8(pf[g][ps], rs[g]);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) l[g] += rs[g];
+  };
+
+  f32x16 sa[G], sb[G];
+  v8 pfa[G][2], pfb[G][2];
+  // One iteration: tile t's V (vb) and tile t+1's K (kb). On entry sb holds
+  // S of half 2t+1 and pfa P of half 2t; on exit sb holds S of half 2t+3 and
+  // pfa P of half 2t+2.
+  auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next,
+                       auto mask_a, auto mask_b) __attribute__((always_inline)) {
+    if constexpr (decltype(has_next)::value) scores(kb, 0, sa);
+    pv(vb, 0, pfa);
+    probs(sb, pfb, BC * t + 32, mask_a);
+    if constexpr (decltype(has_next)::value) scores(kb, 1, sb);
+    pv(vb, 1, pfb);
+    if constexpr (decltype(has_next)::value) probs(sa, pfa, BC * (t + 1), mask_b);
+  };
+  // K tile j lives in buffer j % NB, V tile j in buffer j % NB. Iteration t
+  // reads K t+1 and V t and refills the buffers of K t (with K t+NB) and of
+  // V t-1 (with V t+NB-1), so every copy has NB-1 iterations to land; at the
+  // end of iteration t only the copies of the last NB-2 iterations may still
+  // be in flight. Copies past the end have an empty byte range and move
+  // nothing, which keeps those counts exact.
+  constexpr int KEEP = (NB - 2) * 2 * NDMA;
+  auto copies = [&](int t, unsigned char* kx, unsigned char* vx) __attribute__((always_inline)) {
+    copy_tile(Kh, t + NB, kx, std::false_type{});
+    copy_tile(Vh, t + NB - 1, vx, std::true_type{});
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    wait_vmem_keep<KEEP>();
+    __syncthreads();
+  };
+
+  copy_tile(Kh, 0, k0s, std::false_type{});
+#pragma unroll
+  for (int j = 1; j < NB; ++j) {
+    copy_tile(Kh, j, kbuf(j), std::false_type{});
+    copy_tile(Vh, j - 1, vbuf(j - 1), std::true_type{});
+  }
+  sync();
+  if (rr.wnt > 0) {
+    scores(k0s, 0, sa);
+    scores(k0s, 1, sb);
+    if (0 < rr.wfull) probs(sa, pfa, 0, std::false_type{});
+    else probs(sa, pfa, 0, std::true_type{});
+  }
+  __syncthreads();  // K of tile 0 is read by every wave before its buffer is refilled
+  // Iterations [0, ts): every half unmasked and a next tile to score; NB of
+  // them per pass so that every buffer is named at compile time.
+  const int ts = max(0, rr.wfull - 1);
+  int t = 0;
+  for (; t + NB <= ts; t += NB) {
+    static_for<NB>([&](auto P) __attribute__((always_inline)) {
+      constexpr int q = decltype(P)::value;
+      copies(t + q, kbuf(q), vbuf((q + NB - 1) % NB));
+      iteration(t + q, kbuf((q + 1) % NB), vbuf(q), std::true_type{}, std::false_type{},
+                std::false_type{});
+      sync();
+    });
+  }
+  // The rest: the last steady iterations, the wave's last tiles (the masked
+  // one among them), then the iterations in which only other waves of the
+  // workgroup still compute.
+  for (; t < rr.nt; ++t) {
+    const int q = t % NB;
+    unsigned char* kb = kbuf(q + 1 == NB ? 0 : q + 1);
+    unsigned char* vb = vbuf(q);
+    copies(t, kbuf(q), vbuf(q == 0 ? NB - 1 : q - 1));
+    // Masks are applied wherever a half may need one (an unneeded mask changes
+    // nothing); three variants keep the code small.
+    if (t < rr.wnt) {
+      if (t + 1 < rr.wfull) iteration(t, kb, vb, std::true_type{}, std::false_type{}, std::false_type{});
+      else if (t + 1 < rr.wnt) iteration(t, kb, vb, std::true_type{}, std::true_type{}, std::true_type{});
+      else iteration(t, kb, vb, std::false_type{}, std::true_type{}, std::false_type{});
+    }
+    sync();
+  }
+  // Every copy has landed and every wave is done with K and V: the buffers
+  // now stage O (8 KB per wave for D = 128, two waves per buffer).
+  wait_vmem();
+  __syncthreads();
+  static_assert(NW * G <= 8 && TB >= 2 * 32 * D * 2, "O staging space");
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int slot = wave * G + g;
+    unsigned char* stage = (slot < 2 ? k0s : slot < 4 ? k1s : slot < 6 ? v0s : v1s) +
+                           (slot & 1) * (32 * D * 2);
+    epilogue_staged<T, D, DB>(p, rr.bh, rr.qw0 + 32 * g, lane, m[g], l[g], o[g], stage);
+  }
+  __syncthreads();  // staging reads done before the next tile's copies land
+  };
+
+  // Causal work is folded: a workgroup takes query tile n_qt-1-u and then
+  // tile u of one head, so every workgroup streams n_qt+1 key-tile runs and
+  // the launch needs no longest-first order to stay balanced; the workgroups
+  // are then issued head by head, and those that run together on an XCD
+  // stream the same heads' K/V through its L2. The middle tile of an odd
+  // n_qt is one workgroup's only tile.
+  const int units = CAUSAL ? (p.n_qt + 1) / 2 : p.n_qt;
+  const int bid = blockIdx.x, total = gridDim.x;
+  int logical = bid;
+  if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+  const int bh = logical / units, u = logical - bh * units;
+  const int items = CAUSAL && u != p.n_qt - 1 - u ? 2 : 1;
+#pragma nounroll
+  for (int it = 0; it < items; ++it) process(bh, CAUSAL && it == 0 ? p.n_qt - 1 - u : u);
+}
+
 // ---------------------------------------------------------------------------
 // fp8 e4m3 kernel: S^T on the fp8 matrix cores (32x32x64), P V in bf16.
 // V's fp8 codes are widened to bf16 exactly when staged into LDS (every e4m3
@@ -943,8 +1374,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
 constexpr int kWaves = FA_WAVES;  // x 32 query rows per workgroup
 
 template <class K>
-hipError_t launch(K kernel, const Params& p, int threads, hipStream_t stream) {
-  const long long grid = (long long)p.B * p.H * p.n_qt;
+hipError_t launch(K kernel, const Params& p, int threads, hipStream_t stream, int units = 0) {
+  // units: workgroups per (batch, head); one per query tile unless given
+  const long long grid = (long long)p.B * p.H * (units > 0 ? units : p.n_qt);
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   Params local = p;
   void* args[] = {&local};
@@ -952,21 +1384,39 @@ hipError_t launch(K kernel, const Params& p, int threads, hipStream_t stream) {
                          stream);
 }
 
+// 16-bit kernel choice. The pipelined kernel (FA_WIDE_WAVES * 32 query rows
+// per workgroup) wins without a causal mask and, with one, once the sequence
+// gives every workgroup a long run of key tiles; short causal sequences keep
+// the direct-to-LDS kernel, whose smaller workgroups spread the little work
+// of the short query tiles over more CUs (measured on MI355X).
+bool use_pipe(int N, bool causal) {
+#if FA_16BIT_KERNEL == 3
+  return !causal || N >= FA_PIPE_MIN_N;
+#else
+  (void)N, (void)causal;
+  return FA_16BIT_KERNEL == 2;
+#endif
+}
+
+template <class E, int D, bool C>
+hipError_t launch_16bit(const Params& p, hipStream_t s) {
+  if (use_pipe(p.N, C))
+    return launch(attn_fwd_16bit_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C>, p,
+                  FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
+#if FA_16BIT_KERNEL == 0
+  return launch(attn_fwd_16bit<E, D, kWaves, FA_KEY_TILE, C>, p, kWaves * 64, s);
+#else
+  return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C>, p,
+                FA_DMA_WAVES * 64, s);
+#endif
+}
+
 template <int D, bool C>
 hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
   constexpr int T = kWaves * 64;
   switch (kind) {
-#if FA_16BIT_KERNEL == 1
-    case Kind::BF16:
-      return launch(attn_fwd_16bit_dma<Bf16, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C>, p,
-                    FA_DMA_WAVES * 64, s);
-    case Kind::F16:
-      return launch(attn_fwd_16bit_dma<F16, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C>, p,
-                    FA_DMA_WAVES * 64, s);
-#else
-    case Kind::BF16: return launch(attn_fwd_16bit<Bf16, D, kWaves, FA_KEY_TILE, C>, p, T, s);
-    case Kind::F16: return launch(attn_fwd_16bit<F16, D, kWaves, FA_KEY_TILE, C>, p, T, s);
-#endif
+    case Kind::BF16: return launch_16bit<Bf16, D, C>(p, s);
+    case Kind::F16: return launch_16bit<F16, D, C>(p, s);
     case Kind::FP8: return launch(attn_fwd_fp8<D, kWaves, FA_KEY_TILE, C>, p, T, s);
     case Kind::F32: return launch(attn_fwd_f32<D, kWaves, 32, C>, p, T, s);
   }
@@ -975,11 +1425,14 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
 
 }  // namespace
 
-int rows_per_block(Kind kind, int d) {
+int rows_per_block(Kind kind, int d, int N, bool causal) {
   if (d != 64 && d != 128) return 0;
-#if FA_16BIT_KERNEL == 1
-  if (kind == Kind::BF16 || kind == Kind::F16) return FA_DMA_WAVES * 32;
+  if (kind == Kind::BF16 || kind == Kind::F16) {
+    if (use_pipe(N, causal)) return FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS;
+#if FA_16BIT_KERNEL != 0
+    return FA_DMA_WAVES * 32;
 #endif
+  }
   return kWaves * 32;
 }
 

@@ -24,8 +24,9 @@ struct Params {
 
 enum class Kind { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 
-// Rows of Q owned by one workgroup for a (kind, d) pair; 0 if unsupported.
-int rows_per_block(Kind kind, int d);
+// Rows of Q owned by one workgroup for a problem's kind, d, N and mask; 0 if
+// d is unsupported. Must agree with the kernel launch_forward picks.
+int rows_per_block(Kind kind, int d, int N, bool causal);
 
 // Enqueue the forward on `stream`. Arguments are already validated and
 // p.n_qt filled in. Returns the launch's hipError_t.

@@ -19,6 +19,13 @@ Scores are kept in base 2 with ``scale * log2(e)`` folded into one factor,
 blocks that a causal or padding mask leaves empty are skipped, and the output
 accumulator is rescaled only when a row's running maximum grows. All of that is
 an implementation choice that the tests check leaves the result unchanged.
+
+``move_bound`` models a lazier reference: a row's reference maximum is moved
+(to the running maximum) only when the block's exponentials, taken against the
+current reference, sum to more than ``move_bound`` or to inf/NaN; otherwise the
+stale reference is kept and the exponentials may exceed 1. The output and the
+sum share every scale factor, so the result is the same softmax for any
+reference; the tests check that too.
 """
 from __future__ import annotations
 
@@ -30,7 +37,7 @@ LOG2E = 1.0 / math.log(2.0)
 
 
 def online_forward(q, k, v, scale: float, causal: bool = False, key_len=None,
-                   block_q: int = 64, block_k: int = 64):
+                   block_q: int = 64, block_k: int = 64, move_bound=None):
     """(O, LSE) of the tiled online-softmax algorithm, float64, inputs [B,H,N,d]."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -59,6 +66,12 @@ def online_forward(q, k, v, scale: float, causal: bool = False, key_len=None,
                         ok = ok & (cols[None, :] <= rows[:, None])
                     t = np.where(ok, t, -np.inf)
                     m_new = np.maximum(m, t.max(axis=1))
+                    if move_bound is not None:
+                        # keep the stale reference where its exponentials stay in range
+                        with np.errstate(invalid="ignore", over="ignore"):
+                            s_old = np.exp2(t - m[:, None]).sum(axis=1)
+                        keep = np.isfinite(m) & (s_old <= move_bound)
+                        m_new = np.where(keep, m, m_new)
                     live = np.isfinite(m_new)
                     base = np.where(live, m_new, 0.0)
                     grew = m_new > m

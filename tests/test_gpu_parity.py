@@ -52,6 +52,50 @@ def test_small_shape_sweep(dtype, d, causal):
             assert_close(o, lse, o_ref, lse_ref, dtype, f"N={N} padded={padded}")
 
 
+# Sequences from 4096 keys on run the pipelined 16-bit kernel (256 query rows
+# per workgroup); these cover it with one or two heads, so the full oracle
+# stays cheap: exact multiples of its tiles, ragged ends, padding and causal
+# masks, both head sizes.
+LONG_N = [(4096, False), (4161, True), (4416, False)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_sweep(dtype, d, causal):
+    for i, (N, padded) in enumerate(LONG_N):
+        spec = small_spec(dtype, d, N, causal, padded, B=2 if padded else 1, H=1,
+                          seed=9100 + 13 * i + 2 * d + causal)
+        say(f"case long dtype={dtype} d={d} causal={causal} N={N} padded={padded} seed={spec.seed}")
+        w = W.draw(spec)
+        o, lse = run(w)
+        o_ref, lse_ref = full_oracle(w)
+        assert_close(o, lse, o_ref, lse_ref, dtype, f"N={N} padded={padded}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_long_sequence_growing_and_degenerate(dtype):
+    """The pipelined kernel's lazy reference maximum under keys that grow
+    along the sequence (many reference moves), and degenerate key lengths."""
+    spec = small_spec(dtype, 128, 4224, True, True, B=1, H=2, seed=9300, outliers=False)
+    w = W.draw(spec)
+    grow = torch.linspace(0.2, 40.0, spec.N).reshape(1, 1, spec.N, 1)  # logits reach ~100
+    w.k = (w.k.to(torch.float32) * grow).to(w.k.dtype)
+    say(f"case long growing logits dtype={dtype}")
+    o, lse = run(w)
+    o_ref, lse_ref = full_oracle(w)
+    assert_close(o, lse, o_ref, lse_ref, dtype, "long growing")
+
+    spec = small_spec(dtype, 64, 4100, True, False, B=5, H=1, seed=9301)
+    w = W.draw(spec)
+    w.key_len = np.array([0, 1, -7, 10000, 4033], dtype=np.int32)
+    say(f"case long degenerate key_len dtype={dtype}")
+    o, lse = run(w)
+    o_ref, lse_ref = full_oracle(w)
+    assert np.all(o[0] == 0) and np.all(lse[0] == -np.inf) and np.all(lse[2] == -np.inf)
+    assert_close(o, lse, o_ref, lse_ref, dtype, "long degenerate")
+
+
 def test_fp32_outlier_keys():
     """fp32 with x8 outlier keys: the logits reach ~30 and a 128-term fp32 dot
     product carries ~1e-6 relative rounding, so exp(logit) is off by up to
