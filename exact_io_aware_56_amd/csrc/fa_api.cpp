@@ -43,6 +43,9 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   const __int128 elems = (__int128)B * H * N * d;
   if (elems * 4 > (__int128)INT64_MAX) return fail(FA_ERR_INVALID_ARG, "B*H*N*d overflows");
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  // Kernels address one head's K and V through 32-bit byte offsets.
+  const long long head_bytes = (long long)N * d * (dtype == FA_DTYPE_FP32 ? 4 : dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2);
+  if (head_bytes >= (1LL << 30)) return fail(FA_ERR_UNSUPPORTED, "one head's N x d tensor must be under 1 GiB");
 
   const fa::Kind kind = static_cast<fa::Kind>(dtype);
   const int rows = fa::rows_per_block(kind, d, N, causal != 0);

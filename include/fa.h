@@ -60,7 +60,8 @@ typedef enum {
                               out-of-range dtype, a scale or descale that is
                               not finite and > 0, or sizes whose products
                               overflow                                      */
-  FA_ERR_UNSUPPORTED = -2, /* a head dimension d other than 64 or 128       */
+  FA_ERR_UNSUPPORTED = -2, /* a head dimension d other than 64 or 128, or
+                              one head's N x d tensor of 1 GiB or more      */
   FA_ERR_HIP = -3          /* the HIP runtime refused the launch            */
 } fa_status;
 
@@ -71,7 +72,8 @@ typedef enum {
  *   O        [out] device, [B,H,N,d]; of `dtype`, or bfloat16 for fp8 input
  *   LSE      [out] device, float [B,H,N], natural-log log-sum-exp per row
  *   B, H, N  batch, heads, sequence length (queries and keys), each >= 1
- *   d        head dimension; 64 or 128
+ *   d        head dimension; 64 or 128 (and N*d*sizeof(element) < 2^30:
+ *            one head's Q, K or V below 1 GiB)
  *   scale    multiplies QK^T before the mask; finite and > 0 (the pages use
  *            1/sqrt(d))
  *   causal   0 or 1 (any non-zero value means 1)

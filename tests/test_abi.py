@@ -60,6 +60,8 @@ def call(**kw):
     (dict(o=P + 4), -1), (dict(lse=P + 2), -1), (dict(key_len=P + 1), -1),
     (dict(B=1 << 30, H=1 << 30, N=1 << 30), -1), (dict(d=96), -2), (dict(d=256), -2),
     (dict(d=32, dtype=0), -2),
+    # one head's N x d tensor must stay under 1 GiB: 2^22 rows x 128 x bf16 is exactly 1 GiB
+    (dict(N=1 << 22, d=128), -2), (dict(N=(1 << 21) + 1, d=128, dtype=0), -2),
 ])
 def test_invalid_arguments_are_rejected_on_host(kw, status):
     assert call(**kw) == status
