@@ -90,20 +90,11 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_WIDE_WAVES
 #define FA_WIDE_WAVES 8  // waves per workgroup of the pipelined kernel
 #endif
+#ifndef FA_PIPE_LOOKAHEAD
+#define FA_PIPE_LOOKAHEAD 1  // pipelined kernel: LDS operand reads issued this many MFMAs ahead
+#endif
 #ifndef FA_PIPE_NBUF
 #define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
-#endif
-#ifndef FA_PIPE_PRIO
-#define FA_PIPE_PRIO 0  // pipelined kernel: raise the wave's issue priority around its MFMAs
-#endif
-#ifndef FA_PIPE_FUSED
-#define FA_PIPE_FUSED 0  // pipelined kernel: 1 = instruction order of each step fixed in the source
-#endif
-#ifndef FA_PIPE_SCHED
-#define FA_PIPE_SCHED 0  // VALU instructions placed after each MFMA of a pipeline step (0: compiler's order)
-#endif
-#ifndef FA_PIPE_SCHED_DS
-#define FA_PIPE_SCHED_DS 2  // LDS reads placed after each MFMA when FA_PIPE_SCHED is set
 #endif
 #ifndef FA_WIDE_GROUPS
 #define FA_WIDE_GROUPS 1  // 32-row groups per wave of the pipelined kernel (1 or 2)
@@ -264,9 +255,6 @@ struct Bf16 {
   }
   static __device__ __forceinline__ T cvt(float x) { return (T)x; }
   // acc + sum of the 8 (already rounded) values, fp32 accumulation
-  static __device__ __forceinline__ float sum2(T a, T b, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a, b}, bf16x2{(T)1.0f, (T)1.0f}, acc, false);
-  }
   static __device__ __forceinline__ float sum8(v8 x, float acc) {
     const bf16x2 one = {(T)1.0f, (T)1.0f};
 #pragma unroll
@@ -288,9 +276,6 @@ struct F16 {
     return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)lds));
   }
   static __device__ __forceinline__ T cvt(float x) { return (T)x; }
-  static __device__ __forceinline__ float sum2(T a, T b, float acc) {
-    return __builtin_amdgcn_fdot2(f16x2{a, b}, f16x2{(T)1.0f, (T)1.0f}, acc, false);
-  }
   static __device__ __forceinline__ float sum8(v8 x, float acc) {
     const f16x2 one = {(T)1.0f, (T)1.0f};
 #pragma unroll
@@ -833,7 +818,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
   constexpr int TB = BC * RB;  // bytes per tile
   constexpr int NDMA = TB / (1024 * NW);
   constexpr int NPV = 2 * DB;  // PV MFMA steps per half (2 x 16 keys)
-  constexpr int LA = FA_LOOKAHEAD;
+  constexpr int LA = FA_PIPE_LOOKAHEAD;
   static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB copies per wave");
   static_assert(NB >= 2 && NB <= 4, "two to four LDS buffers per operand");
 
@@ -926,9 +911,6 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
   };
   // S^T = K Q^T over one 32-key half for every group, each K operand read once
   auto scores = [&](const unsigned char* kb, int h, f32x16 (&s)[G]) __attribute__((always_inline)) {
-#if FA_PIPE_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = f32x16{};
     v8 ring[LA + 1];
@@ -940,9 +922,6 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] = E::mma(ring[u % (LA + 1)], qf[g][u], s[g]);
     }
-#if FA_PIPE_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
   };
 
   f32x16 o[G][DB];
@@ -958,9 +937,6 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
 
   // O += V^T P^T over one 32-key half, each V operand read once
   auto pv = [&](const unsigned char* vb, int h, const v8 (&pf)[G][2]) __attribute__((always_inline)) {
-#if FA_PIPE_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
     v8 ring[LA + 1];
 #pragma unroll
     for (int t = 0; t < NPV + LA; ++t) {
@@ -970,9 +946,6 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
 #pragma unroll
         for (int g = 0; g < G; ++g) o[g][u % DB] = E::mma(ring[u % (LA + 1)], pf[g][u / DB], o[g][u % DB]);
     }
-#if FA_PIPE_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
   };
   // P of one half from its raw scores s (k0 = its first key); updates l and,
   // on the rare branch, m, base and O.
@@ -1019,39 +992,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
       }
       bad |= !(rs[g] <= E::kPBound);
     }
-#if FA_PIPE_SCHED
-    // Spread the step's vector work and LDS reads evenly between its MFMAs.
-    static_for<2 * KS * G>([&](auto) __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, FA_PIPE_SCHED_DS, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, FA_PIPE_SCHED, 0);  // VALU
-    });
-#endif
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float x = s[g][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) x = fmaxf(x, s[g][i]);
-        const float mn = fmaxf(m[g], max_halves(x));
-        const float alpha = pinned(mn == m[g] ? 1.0f : fast_exp2((m[g] - mn) * c));
-        l[g] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha;
-        m[g] = mn;
-        base[g] = -mn * c;
-        const float bu = mn == -INFINITY ? 0.0f : base[g];
-        rs[g] = 0.0f;
-#pragma unroll
-        for (int ps = 0; ps < 2; ++ps) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[g][ps][e] = E::cvt(fast_exp2(fmaf(s[g][8 * ps + e], c, bu)));
-          rs[g] = E::sum8(pf[g][ps], rs[g]);
-        }
-      }
-    }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) fix_probs(s, pf, rs);
 #pragma unroll
     for (int g = 0; g < G; ++g) l[g] += rs[g];
   };
@@ -1061,81 +1002,6 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
   // One iteration: tile t's V (vb) and tile t+1's K (kb). On entry sb holds
   // S of half 2t+1 and pfa P of half 2t; on exit sb holds S of half 2t+3 and
   // pfa P of half 2t+2.
-#if FA_PIPE_FUSED
-  // One pipeline step with its instruction order fixed in the source. Slot u
-  // (KS slots: the S and the PV products of a half both take KS MFMA steps)
-  // reads the K and V operands of slot u+LA, issues S MFMA u of the next half
-  // (into sn) and PV MFMA u of the previous half (P in pfp), and turns 16/KS
-  // scores of this half (sc) into P (pfn); a scheduling barrier closes each
-  // slot, so the matrix and vector work stay interleaved.
-  auto fstep = [&](const unsigned char* kb, int kh, const unsigned char* vb, int vh,
-                   f32x16 (&sc)[G], f32x16 (&sn)[G], const v8 (&pfp)[G][2], v8 (&pfn)[G][2],
-                   int k0, auto has_s, auto has_p, auto masked) __attribute__((always_inline)) {
-    constexpr bool HS = decltype(has_s)::value, HP = decltype(has_p)::value;
-    constexpr int EPS = 16 / KS;  // scores per slot and lane
-    if constexpr (HP && decltype(masked)::value)
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        apply_mask<1, CAUSAL>(*reinterpret_cast<f32x16(*)[1]>(&sc[g]), k0, rr.kl, rr.qrow + 32 * g, hi);
-    if constexpr (HS)
-#pragma unroll
-      for (int g = 0; g < G; ++g) sn[g] = f32x16{};
-    float rs[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) rs[g] = 0.0f;
-    v8 kr[LA + 1], vr[LA + 1];
-#pragma unroll
-    for (int t = 0; t < LA; ++t) {
-      if constexpr (HS) kr[t] = kfrag(kb, kh, t);
-      vr[t] = vfrag(vb, vh, t);
-    }
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      if (u + LA < KS) {
-        if constexpr (HS) kr[(u + LA) % (LA + 1)] = kfrag(kb, kh, u + LA);
-        vr[(u + LA) % (LA + 1)] = vfrag(vb, vh, u + LA);
-      }
-#if FA_PIPE_PRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
-      if constexpr (HS)
-#pragma unroll
-        for (int g = 0; g < G; ++g) sn[g] = E::mma(kr[u % (LA + 1)], qf[g][u], sn[g]);
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        o[g][u % DB] = E::mma(vr[u % (LA + 1)], pfp[g][u / DB], o[g][u % DB]);
-#if FA_PIPE_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
-      if constexpr (HP)
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < EPS; e += 2) {
-            const int i = u * EPS + e;
-            const T a = E::cvt(fast_exp2(fmaf(sc[g][i], c, base[g])));
-            const T b = E::cvt(fast_exp2(fmaf(sc[g][i + 1], c, base[g])));
-            pfn[g][i / 8][i % 8] = a;
-            pfn[g][i / 8][i % 8 + 1] = b;
-            rs[g] = E::sum2(a, b, rs[g]);
-          }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (HP) {
-      bool bad = false;
-#pragma unroll
-      for (int g = 0; g < G; ++g) bad |= !(rs[g] <= E::kPBound);
-      if (__builtin_amdgcn_ballot_w64(bad) != 0) fix_probs(sc, pfn, rs);
-#pragma unroll
-      for (int g = 0; g < G; ++g) l[g] += rs[g];
-    }
-  };
-  auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next,
-                       auto mask_a, auto mask_b) __attribute__((always_inline)) {
-    fstep(kb, 0, vb, 0, sb, sa, pfa, pfb, BC * t + 32, has_next, std::true_type{}, mask_a);
-    fstep(kb, 1, vb, 1, sa, sb, pfb, pfa, BC * (t + 1), has_next, has_next, mask_b);
-  };
-#else
   auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next,
                        auto mask_a, auto mask_b) __attribute__((always_inline)) {
     if constexpr (decltype(has_next)::value) scores(kb, 0, sa);
@@ -1145,7 +1011,6 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
     pv(vb, 1, pfb);
     if constexpr (decltype(has_next)::value) probs(sa, pfa, BC * (t + 1), mask_b);
   };
-#endif
   // K tile j lives in buffer j % NB, V tile j in buffer j % NB. Iteration t
   // reads K t+1 and V t and refills the buffers of K t (with K t+NB) and of
   // V t-1 (with V t+NB-1), so every copy has NB-1 iterations to land; at the
@@ -1191,14 +1056,13 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
   }
   // The rest: the last steady iterations, the wave's last tiles (the masked
   // one among them), then the iterations in which only other waves of the
-  // workgroup still compute.
+  // workgroup still compute. Masks are applied wherever a half may need one
+  // (an unneeded mask changes nothing); three variants keep the code small.
   for (; t < rr.nt; ++t) {
     const int q = t % NB;
     unsigned char* kb = kbuf(q + 1 == NB ? 0 : q + 1);
     unsigned char* vb = vbuf(q);
     copies(t, kbuf(q), vbuf(q == 0 ? NB - 1 : q - 1));
-    // Masks are applied wherever a half may need one (an unneeded mask changes
-    // nothing); three variants keep the code small.
     if (t < rr.wnt) {
       if (t + 1 < rr.wfull) iteration(t, kb, vb, std::true_type{}, std::false_type{}, std::false_type{});
       else if (t + 1 < rr.wnt) iteration(t, kb, vb, std::true_type{}, std::true_type{}, std::true_type{});
