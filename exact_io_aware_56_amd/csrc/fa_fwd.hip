@@ -574,10 +574,28 @@ template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   return r & (D / 8 - 1);
 }
+// fp8 K rows (D bytes, D/16 slots): the 16 rows a quarter-wave reads at one
+// logical slot land on 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k8_swz(int r) {
+  if constexpr (D == 128) return (r >> 1) & 7;
+  return (r >> 2) & 3;
+}
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
   if constexpr (D == 128) return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0);
   return (r & 3) << 1;
+}
+
+// Four e4m3 codes -> four bf16 (exact): hardware fp8->f32 convert, keep the
+// high halves (an e4m3 value has at most 4 significant bits).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(unsigned w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2 r;
+  r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+  r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+  return r;
 }
 
 // 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane (dst is
@@ -802,24 +820,29 @@ __device__ __forceinline__ void static_for(F&& f) {
 // range, see row_range), and it is the wave's last tile.
 // ---------------------------------------------------------------------------
 
-template <class E, int D, int G, int NW, int NB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) {
-  using T = typename E::T;
+template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8>
+__global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
+  using T = typename E::T;  // P, V in LDS and O (bfloat16 for fp8 inputs)
   using v8 = typename E::v8;
   using v4 = typename E::v4;
+  using QT = std::conditional_t<F8, i32x8, v8>;  // one Q or K operand of the S product
   static_assert(G == 1 || G == 2, "one or two 32-row groups per wave");
+  static_assert(!F8 || (G == 1 && NB == 2), "fp8 inputs: one row group, two buffers");
   constexpr int WR = 32 * G;   // query rows per wave
   constexpr int BR = NW * WR;  // query rows per workgroup
   constexpr int BC = 64;       // keys per LDS tile
-  constexpr int KS = D / 16;   // MFMA steps over the head dim
+  constexpr int KS = F8 ? D / 64 : D / 16;  // S MFMA steps over the head dim
   constexpr int DB = D / 32;   // 32-wide head-dim blocks of O^T
-  constexpr int RB = D * 2;    // bytes per K / V row
-  constexpr int CPR = D / 8;   // 16-byte slots per row
-  constexpr int TB = BC * RB;  // bytes per tile
-  constexpr int NDMA = TB / (1024 * NW);
+  constexpr int RB = D * 2;    // bytes per 16-bit V (and 16-bit K) row in LDS
+  constexpr int KRB = F8 ? D : RB;  // bytes per K row (global and LDS)
+  constexpr int CPR = D / 8;   // 16-byte slots per 16-bit row
+  constexpr int KCPR = KRB / 16;    // 16-byte slots per K row
+  constexpr int TB = BC * RB;  // bytes per 16-bit tile (every LDS buffer's size)
+  constexpr int NKC = BC * KRB / 1024;  // 1 KB copies per K tile
+  constexpr int NDMA = (NKC + NW - 1) / NW;  // K copies per wave per tile (some idle when ragged)
   constexpr int NPV = 2 * DB;  // PV MFMA steps per half (2 x 16 keys)
   constexpr int LA = FA_PIPE_LOOKAHEAD;
-  static_assert(TB % (1024 * NW) == 0, "tile must split into 1 KB copies per wave");
+  static_assert(F8 || NKC % NW == 0, "16-bit tiles must split into 1 KB copies per wave");
   static_assert(NB >= 2 && NB <= 4, "two to four LDS buffers per operand");
 
   // One named array per buffer: distinct objects let the compiler see that a
@@ -850,10 +873,19 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
   // Lane-derived offsets are recomputed per tile from an opaque copy of the
   // lane index, so that they are not kept live (and spilled) across tiles.
   const int ln = pinned_int(lane);
-  int koff[KS];
+  // K operand addresses: 16-bit, one 16-byte slot per MFMA step; fp8, two.
+  int koff[F8 ? 2 * KS : KS];
+  if constexpr (F8) {
 #pragma unroll
-  for (int st = 0; st < KS; ++st)
-    koff[st] = (ln & 31) * RB + (((2 * st + (ln >> 5)) ^ k_swz<D>(ln & 31)) << 4);
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        koff[2 * st + x] = (ln & 31) * KRB + (((4 * st + 2 * (ln >> 5) + x) ^ k8_swz<D>(ln & 31)) << 4);
+  } else {
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      koff[st] = (ln & 31) * RB + (((2 * st + (ln >> 5)) ^ k_swz<D>(ln & 31)) << 4);
+  }
   int voff[DB];
   {
     const int g = ln >> 4, i = ln & 15;
@@ -865,41 +897,82 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
     }
   }
   const RowRange rr = row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
-  const size_t head = (size_t)rr.bh * N * D;
-  const T* Kh = (const T*)p.k + head;
-  const T* Vh = (const T*)p.v + head;
+  const size_t head = (size_t)rr.bh * N * D;  // elements
+  const unsigned char* Qh = (const unsigned char*)p.q + head * (KRB / D);
+  const unsigned char* Kh = (const unsigned char*)p.k + head * (KRB / D);
+  const unsigned char* Vh = (const unsigned char*)p.v + head * (KRB / D);
 
-  v8 qf[G][KS];
+  // Q^T operand: lane holds its query row's head-dim elements
+  // [16*st + 8*hi, +8) (16-bit) or [64*st + 32*hi, +32) (fp8).
+  QT qf[G][KS];
   {
-    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, RB);
+    const auto rq = tile_rsrc(Qh, rr.q_wg0 / BR, BR, N, KRB);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int off = ((rr.qrow + 32 * g - rr.q_wg0) * D + 8 * hi) * 2;
+      const int row = rr.qrow + 32 * g - rr.q_wg0;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[g][s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (F8) {
+          const int off = row * KRB + 64 * s + 32 * hi;
+          qf[g][s] = __builtin_shufflevector(load16(rq, off), load16(rq, off + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          qf[g][s] = __builtin_bit_cast(v8, load16(rq, row * KRB + 32 * s + 16 * hi));
+        }
+      }
     }
   }
   // One buffer resource per operand over the head's first kl key rows (the
-  // host keeps a head under 2 GiB): a tile's copy only adds its byte offset,
+  // host keeps a head under 1 GiB): a tile's copy only adds its byte offset,
   // and rows at or beyond kl (a ragged last tile, tiles past the end) read
   // as zeros.
-  const auto rsK = buffer_rsrc(Kh, rr.kl * RB);
-  const auto rsV = buffer_rsrc(Vh, rr.kl * RB);
-  auto copy_tile = [&](const T* xh, int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
-    (void)xh;
+  const auto rsK = buffer_rsrc(Kh, rr.kl * KRB);
+  const auto rsV = buffer_rsrc(Vh, rr.kl * KRB);
+  // K tile j (and V tile j for 16-bit inputs) straight into LDS, 16-byte
+  // slots permuted per row as the operand reads expect.
+  auto copy_tile = [&](int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
+    constexpr bool IV = decltype(is_v)::value;
+    constexpr int cpr = IV ? CPR : KCPR, rb = IV ? RB : KRB;
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       const int blk = c * NW + wave;
-      const int slot = blk * 64 + lane;
-      const int r = slot / CPR, ps = slot % CPR;
-      const int lc = ps ^ (decltype(is_v)::value ? v_swz<D>(r) : k_swz<D>(r));
-      lds_copy16(decltype(is_v)::value ? rsV : rsK, dst + blk * 1024,
-                 j * (BC * RB) + r * RB + (lc << 4));
+      if (NKC % NW == 0 || blk < NKC) {
+        const int slot = blk * 64 + lane;
+        const int r = slot / cpr, ps = slot % cpr;
+        const int lc = ps ^ (IV ? v_swz<D>(r) : F8 ? k8_swz<D>(r) : k_swz<D>(r));
+        lds_copy16(IV ? rsV : rsK, dst + blk * 1024, j * (BC * rb) + r * rb + (lc << 4));
+      }
     }
   };
-  // K operand of MFMA step st over keys [32*h, 32*h + 32) of the tile at kb
-  auto kfrag = [&](const unsigned char* kb, int h, int st) __attribute__((always_inline)) {
-    return *(const v8*)(kb + 32 * h * RB + koff[st]);
+  // fp8 V: this lane's 16 codes of the tile in flight, widened to bf16
+  // (exactly) and stored into the 16-bit V layout at the end of the iteration.
+  constexpr int VSLOTS = BC * D / 16;  // 16-code pieces per fp8 V tile
+  const int vslot = wave * 64 + lane;
+  i32x4 vreg = {};
+  auto vload = [&](int j) __attribute__((always_inline)) {
+    if (vslot < VSLOTS) vreg = load16(rsV, j * (BC * D) + vslot * 16);
+  };
+  auto vstore = [&](unsigned char* dst) __attribute__((always_inline)) {
+    if (vslot < VSLOTS) {
+      const int r = vslot / (D / 16), cc = vslot % (D / 16);
+      i32x4 w0, w1;
+      u32x2 t;
+      t = fp8x4_to_bf16x4((unsigned)vreg[0]); w0[0] = t[0]; w0[1] = t[1];
+      t = fp8x4_to_bf16x4((unsigned)vreg[1]); w0[2] = t[0]; w0[3] = t[1];
+      t = fp8x4_to_bf16x4((unsigned)vreg[2]); w1[0] = t[0]; w1[1] = t[1];
+      t = fp8x4_to_bf16x4((unsigned)vreg[3]); w1[2] = t[0]; w1[3] = t[1];
+      *(i32x4*)(dst + r * RB + (((2 * cc) ^ v_swz<D>(r)) << 4)) = w0;
+      *(i32x4*)(dst + r * RB + (((2 * cc + 1) ^ v_swz<D>(r)) << 4)) = w1;
+    }
+  };
+  // K operand of S MFMA step st over keys [32*h, 32*h + 32) of the tile at kb
+  auto kfrag = [&](const unsigned char* kb, int h, int st) __attribute__((always_inline)) -> QT {
+    if constexpr (F8) {
+      const unsigned char* b = kb + 32 * h * KRB;
+      return __builtin_shufflevector(*(const i32x4*)(b + koff[2 * st]),
+                                     *(const i32x4*)(b + koff[2 * st + 1]), 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *(const v8*)(kb + 32 * h * RB + koff[st]);
+    }
   };
   // V^T operand of PV step u = ps*DB + db over keys 32*h + 16*ps + [0, 16)
   auto vfrag = [&](const unsigned char* vb, int h, int u) __attribute__((always_inline)) {
@@ -913,14 +986,20 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
   auto scores = [&](const unsigned char* kb, int h, f32x16 (&s)[G]) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = f32x16{};
-    v8 ring[LA + 1];
+    QT ring[LA + 1];
 #pragma unroll
     for (int t = 0; t < KS + LA; ++t) {
       if (t < KS) ring[t % (LA + 1)] = kfrag(kb, h, t);
       const int u = t - LA;
       if (u >= 0)
 #pragma unroll
-        for (int g = 0; g < G; ++g) s[g] = E::mma(ring[u % (LA + 1)], qf[g][u], s[g]);
+        for (int g = 0; g < G; ++g) {
+          if constexpr (F8)  // formats 0/0: fp8 e4m3 operands; E8M0 scales 127 = 1.0
+            s[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[u % (LA + 1)], qf[g][u], s[g],
+                                                                    0, 0, 0, 127, 0, 127);
+          else
+            s[g] = E::mma(ring[u % (LA + 1)], qf[g][u], s[g]);
+        }
     }
   };
 
@@ -1018,22 +1097,32 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
   // be in flight. Copies past the end have an empty byte range and move
   // nothing, which keeps those counts exact.
   constexpr int KEEP = (NB - 2) * 2 * NDMA;
+  // fp8 V tiles take registers instead: loaded with the copies, stored to
+  // vx just before the iteration's barrier.
   auto copies = [&](int t, unsigned char* kx, unsigned char* vx) __attribute__((always_inline)) {
-    copy_tile(Kh, t + NB, kx, std::false_type{});
-    copy_tile(Vh, t + NB - 1, vx, std::true_type{});
+    copy_tile(t + NB, kx, std::false_type{});
+    if constexpr (F8) vload(t + NB - 1);
+    else copy_tile(t + NB - 1, vx, std::true_type{});
   };
-  auto sync = [&]() __attribute__((always_inline)) {
+  auto sync_after = [&](unsigned char* vx) __attribute__((always_inline)) {
+    if constexpr (F8) vstore(vx);
     wait_vmem_keep<KEEP>();
     __syncthreads();
   };
 
-  copy_tile(Kh, 0, k0s, std::false_type{});
+  copy_tile(0, k0s, std::false_type{});
 #pragma unroll
   for (int j = 1; j < NB; ++j) {
-    copy_tile(Kh, j, kbuf(j), std::false_type{});
-    copy_tile(Vh, j - 1, vbuf(j - 1), std::true_type{});
+    copy_tile(j, kbuf(j), std::false_type{});
+    if constexpr (F8) {
+      vload(j - 1);
+      vstore(vbuf(j - 1));
+    } else {
+      copy_tile(j - 1, vbuf(j - 1), std::true_type{});
+    }
   }
-  sync();
+  wait_vmem_keep<KEEP>();
+  __syncthreads();
   if (rr.wnt > 0) {
     scores(k0s, 0, sa);
     scores(k0s, 1, sb);
@@ -1051,7 +1140,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
       copies(t + q, kbuf(q), vbuf((q + NB - 1) % NB));
       iteration(t + q, kbuf((q + 1) % NB), vbuf(q), std::true_type{}, std::false_type{},
                 std::false_type{});
-      sync();
+      sync_after(vbuf((q + NB - 1) % NB));
     });
   }
   // The rest: the last steady iterations, the wave's last tiles (the masked
@@ -1062,13 +1151,14 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
     const int q = t % NB;
     unsigned char* kb = kbuf(q + 1 == NB ? 0 : q + 1);
     unsigned char* vb = vbuf(q);
-    copies(t, kbuf(q), vbuf(q == 0 ? NB - 1 : q - 1));
+    unsigned char* vx = vbuf(q == 0 ? NB - 1 : q - 1);
+    copies(t, kbuf(q), vx);
     if (t < rr.wnt) {
       if (t + 1 < rr.wfull) iteration(t, kb, vb, std::true_type{}, std::false_type{}, std::false_type{});
       else if (t + 1 < rr.wnt) iteration(t, kb, vb, std::true_type{}, std::true_type{}, std::true_type{});
       else iteration(t, kb, vb, std::false_type{}, std::true_type{}, std::false_type{});
     }
-    sync();
+    sync_after(vx);
   }
   // Every copy has landed and every wave is done with K and V: the buffers
   // now stage O (8 KB per wave for D = 128, two waves per buffer).
@@ -1106,17 +1196,6 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_16bit_pipe(Params p) 
 // V's fp8 codes are widened to bf16 exactly when staged into LDS (every e4m3
 // value is a bf16 value), and P is rounded to bf16 as in the bf16 kernel.
 // ---------------------------------------------------------------------------
-
-// Four e4m3 codes -> four bf16 (exact): hardware fp8->f32 convert, keep the
-// high halves (an e4m3 value has at most 4 significant bits).
-__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(unsigned w) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  u32x2 r;
-  r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-  r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
-  return r;
-}
 
 template <int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, FA_WAVES_PER_EU) void attn_fwd_fp8(Params p) {
@@ -1399,7 +1478,7 @@ bool use_pipe(int N, bool causal) {
 template <class E, int D, bool C>
 hipError_t launch_16bit(const Params& p, hipStream_t s) {
   if (use_pipe(p.N, C))
-    return launch(attn_fwd_16bit_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C>, p,
+    return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false>, p,
                   FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
 #if FA_16BIT_KERNEL == 0
   return launch(attn_fwd_16bit<E, D, kWaves, FA_KEY_TILE, C>, p, kWaves * 64, s);
@@ -1415,7 +1494,11 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
   switch (kind) {
     case Kind::BF16: return launch_16bit<Bf16, D, C>(p, s);
     case Kind::F16: return launch_16bit<F16, D, C>(p, s);
-    case Kind::FP8: return launch(attn_fwd_fp8<D, kWaves, FA_KEY_TILE, C>, p, T, s);
+    case Kind::FP8:
+      if (use_pipe(p.N, C))
+        return launch(attn_fwd_pipe<Bf16, D, 1, FA_WIDE_WAVES, 2, C, true>, p, FA_WIDE_WAVES * 64, s,
+                      C ? (p.n_qt + 1) / 2 : p.n_qt);
+      return launch(attn_fwd_fp8<D, kWaves, FA_KEY_TILE, C>, p, T, s);
     case Kind::F32: return launch(attn_fwd_f32<D, kWaves, 32, C>, p, T, s);
   }
   return hipErrorInvalidValue;
@@ -1425,6 +1508,7 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
 
 int rows_per_block(Kind kind, int d, int N, bool causal) {
   if (d != 64 && d != 128) return 0;
+  if (kind == Kind::FP8 && use_pipe(N, causal)) return FA_WIDE_WAVES * 32;
   if (kind == Kind::BF16 || kind == Kind::F16) {
     if (use_pipe(N, causal)) return FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS;
 #if FA_16BIT_KERNEL != 0
