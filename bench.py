@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s and % of MFMA peak, bf16 causal B1 H32 N8192 d128"
 # Published dense MI355X peaks (TFLOP/s) per input dtype of the contraction.
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp32": 157.3}
+EXP_PEAK_T = 256 * 4 * 8 * 2.4e9 / 1e12
 KERNEL_SOURCES = ["exact_io_aware_56_amd/csrc/fa_fwd.hip", "exact_io_aware_56_amd/csrc/fa_api.cpp",
                   "exact_io_aware_56_amd/csrc/fa_internal.h"]
 
@@ -103,6 +104,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_causal_bf16")
+    ap.add_argument("--N", type=int, default=0,
+                    help="override the workload's sequence length (HBM scaling runs); "
+                         "such a line is not the headline measurement")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -133,6 +137,9 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
         return 0
     spec = W.SPECS[args.workload]
+    default_n = args.N in (0, spec.N)
+    if not default_n:
+        spec = spec.with_shape(N=args.N)
     w = W.draw(spec)
     dev = torch.device("cuda", 0)
     q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
@@ -177,10 +184,11 @@ def main(argv=None):
     value = flop / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[spec.dtype]
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
-    traffic = measured_traffic(spec.name)
+    traffic = measured_traffic(spec.name) if default_n else None
+    exps = spec.exps()
     result = {
-        "metric": METRIC if spec.name == "long_causal_bf16" else
-        f"attention fwd TFLOP/s ({spec.name})",
+        "metric": METRIC if spec.name == "long_causal_bf16" and default_n else
+        f"attention fwd TFLOP/s ({spec.name}, N={spec.N})",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -212,8 +220,16 @@ def main(argv=None):
             "traffic": traffic,
             "algorithmic_bytes": algorithmic_bytes(spec),
             "kernel_sources_sha256_16": kernel_sha(),
+            # Secondary bound: one exp2 per unmasked score on the transcendental
+            # unit (256 CUs x 4 SIMDs x 8 lanes per cycle x 2.4 GHz).
+            "exp": {"achieved": round(exps / (avg_launch_ms * 1e-3) / 1e12, 4),
+                    "peak": EXP_PEAK_T, "unit": "Texp/s",
+                    "frac": round(exps / (avg_launch_ms * 1e-3) / 1e12 / EXP_PEAK_T, 4)},
         },
     }
+    if w.key_len is not None and not spec.causal:
+        eff = spec.flops() * float(w.key_len.sum()) / (spec.B * spec.N)
+        result["config"]["effective_tflops"] = round(eff / (ms_per_step * 1e-3) / 1e12, 3)
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -2,8 +2,8 @@
 
 Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` marshal torch
 tensors' device pointers and the current stream into the C entry points of the
-same names; ``forward`` additionally allocates O and LSE. Nothing here
-computes any part of the attention.
+same names; ``fwd`` (and its positional twin ``forward``) additionally
+allocates O and LSE. Nothing here computes any part of the attention.
 """
 from __future__ import annotations
 
@@ -90,3 +90,16 @@ def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
     else:
         fa_fwd(q, k, v, o, lse, scale, causal, key_len, stream=stream)
     return o, lse
+
+
+def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
+        descale: Tuple[float, float, float] = (1.0, 1.0, 1.0),
+        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """softmax(scale * Q K^T + mask) V and its row log-sum-exp, as (O, LSE).
+
+    Keyword-only form of ``forward``. q, k, v: contiguous device tensors
+    [B, H, N, d] of one dtype (float32, float16, bfloat16 or float8_e4m3fn);
+    key_len: optional device int32 [B] of valid key counts. O has q's dtype
+    (bfloat16 for fp8 inputs); LSE is float32 [B, H, N], natural log.
+    """
+    return forward(q, k, v, scale, causal, key_len, descale, stream)

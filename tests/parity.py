@@ -36,8 +36,8 @@ def to_device(w):
 def run(w, stream=None):
     """Run the library on workload w; returns (O, LSE) as float64 numpy arrays."""
     q, k, v, kl = to_device(w)
-    o, lse = fa.forward(q, k, v, w.spec.scale, w.spec.causal, kl, descale=w.descale,
-                        stream=stream)
+    o, lse = fa.fwd(q, k, v, scale=w.spec.scale, causal=w.spec.causal, key_len=kl,
+                    descale=w.descale, stream=stream)
     torch.cuda.synchronize()
     return o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
 

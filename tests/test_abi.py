@@ -77,3 +77,17 @@ def test_fp8_descales_are_validated():
     # scale * q_descale * k_descale must stay finite
     st = _lib.fa_fwd_fp8_raw(P, P, P, P, P, 1, 1, 16, 128, 3e38, 1, None, 1e10, 1.0, 1.0, None)
     assert st == -1
+
+
+def test_python_binding_names_the_entry_points():
+    import inspect
+
+    import exact_io_aware_56_amd as fa
+
+    assert callable(fa.fa_fwd) and callable(fa.fa_fwd_fp8)
+    sig = inspect.signature(fa.fwd)
+    assert list(sig.parameters)[:3] == ["q", "k", "v"]
+    for name in ("scale", "causal", "key_len"):
+        assert sig.parameters[name].kind is inspect.Parameter.KEYWORD_ONLY, name
+    assert sig.parameters["causal"].default is False
+    assert sig.parameters["key_len"].default is None

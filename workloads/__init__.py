@@ -63,6 +63,11 @@ class Spec:
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
+    def exps(self) -> float:
+        """Nominal exponentials (one per score): B*H*N^2, halved when causal."""
+        e = float(self.B) * self.H * self.N * self.N
+        return e / 2 if self.causal else e
+
     def with_shape(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
 
