@@ -93,6 +93,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_PIPE_LOOKAHEAD
 #define FA_PIPE_LOOKAHEAD 1  // pipelined kernel: LDS operand reads issued this many MFMAs ahead
 #endif
+#ifndef FA_PIPE_IGLP
+#define FA_PIPE_IGLP 3  // pipelined kernel: the compiler's MFMA/exp interleave for each half-step (-1: none)
+#endif
 #ifndef FA_PIPE_NBUF
 #define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
 #endif
@@ -1058,6 +1061,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   auto probs = [&](f32x16 (&s)[G], v8 (&pf)[G][2], int k0, auto masked) __attribute__((always_inline)) {
     float rs[G];
     bool bad = false;
+    if constexpr (FA_PIPE_IGLP >= 0) __builtin_amdgcn_iglp_opt(FA_PIPE_IGLP);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if constexpr (decltype(masked)::value)
