@@ -17,6 +17,12 @@ do not say which masks; this reference takes the additive -inf reading:
     m_i     = max_j s_ij,  e_ij = exp(s_ij - m_i),  l_i = sum_j e_ij
     P_ij    = e_ij / l_i,  O_i = sum_j P_ij V_j,  LSE_i = m_i + log(l_i)
 
+Grouped K/V heads: FlashAttention (ES), "Evolución y desarrollos posteriores",
+lists multi-query attention (one K/V head for all query heads) among
+FlashAttention-2's additions. K and V may therefore carry H_kv heads with H_kv
+dividing H; query head h then takes K/V head h // (H // H_kv) (consecutive
+query heads form a group; H_kv = 1 is multi-query, H_kv = H the plain case).
+
 A row with no allowed key gets O_i = 0 and LSE_i = -inf. key_len is clamped to
 [0, N]; None means every key is valid. LSE is the natural-log log-sum-exp of
 the allowed scaled logits, i.e. the running maximum and running sum of
@@ -82,11 +88,19 @@ def _rows_forward(q_rows, k, v, scale, rows, causal, kl):
     return o, lse
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """The K/V head that query head h of H attends with, for H_kv K/V heads."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError("H_kv must divide H")
+    return h // (H // H_kv)
+
+
 def attention_forward(q, k, v, scale: float, causal: bool = False,
                       key_len: Optional[Sequence[int]] = None, row_block: int = 2048):
-    """O [B,H,N,d] and LSE [B,H,N] (float64) for inputs [B,H,N,d]."""
+    """O [B,H,N,d] and LSE [B,H,N] (float64) for q [B,H,N,d] and k, v [B,H_kv,N,d]."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     o = np.zeros((B, H, N, v.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
@@ -94,8 +108,9 @@ def attention_forward(q, k, v, scale: float, causal: bool = False,
         for h in range(H):
             for r0 in range(0, N, row_block):
                 rows = np.arange(r0, min(N, r0 + row_block))
+                g = kv_head(h, H, H_kv)
                 o[b, h, rows], lse[b, h, rows] = _rows_forward(
-                    q[b, h, rows], k[b, h], v[b, h], scale, rows, causal, kl)
+                    q[b, h, rows], k[b, g], v[b, g], scale, rows, causal, kl)
     return o, lse
 
 
@@ -105,7 +120,8 @@ def attention_rows(q, k, v, scale: float, causal: bool, key_len, b: int, h: int,
     rows = np.asarray(rows, dtype=np.int64)
     N = q.shape[2]
     kl = clamp_key_len(key_len, b, N)
-    return _rows_forward(_as64(q[b, h, rows]), _as64(k[b, h]), _as64(v[b, h]), scale, rows,
+    g = kv_head(h, q.shape[1], k.shape[1])
+    return _rows_forward(_as64(q[b, h, rows]), _as64(k[b, g]), _as64(v[b, g]), scale, rows,
                          causal, kl)
 
 
