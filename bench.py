@@ -61,11 +61,12 @@ def measured_traffic(workload: str):
 
 
 def algorithmic_bytes(spec) -> int:
-    """Q, K, V read once, O written once, LSE written once."""
+    """Q, K, V read once, O written once, LSE written once (K and V have
+    H_kv heads when the workload groups them)."""
     e_in = {"fp32": 4, "fp16": 2, "bf16": 2, "fp8": 1}[spec.dtype]
     e_out = {"fp32": 4, "fp16": 2, "bf16": 2, "fp8": 2}[spec.dtype]
-    n = spec.B * spec.H * spec.N * spec.d
-    return (3 * e_in + e_out) * n + 4 * spec.B * spec.H * spec.N
+    row = spec.B * spec.N * spec.d
+    return ((e_in + e_out) * spec.H + 2 * e_in * spec.kv_heads) * row + 4 * spec.B * spec.H * spec.N
 
 
 def cpu_baseline(w, budget_s: float):
@@ -88,8 +89,9 @@ def cpu_baseline(w, budget_s: float):
     for b in range(s.B):
         for h in range(s.H):
             kb = None if kl is None else kl[b:b + 1]
-            oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
-                                     v[b:b + 1, h:h + 1], s.scale, s.causal, kb)
+            g = h // (s.H // s.kv_heads)
+            oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1],
+                                     v[b:b + 1, g:g + 1], s.scale, s.causal, kb)
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -154,7 +156,9 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
 
     def step():
-        if spec.dtype == "fp8":
+        if spec.kv_heads != spec.H:
+            fa.fa_fwd_gqa(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
+        elif spec.dtype == "fp8":
             fa.fa_fwd_fp8(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
         else:
             fa.fa_fwd(q, k, v, o, lse, spec.scale, spec.causal, kl, stream=stream)
@@ -220,6 +224,7 @@ def main(argv=None):
         "config": {
             "workload": spec.name, "B": spec.B, "H": spec.H, "N": spec.N, "d": spec.d,
             "causal": spec.causal, "scale": spec.scale,
+            "H_kv": spec.kv_heads,
             "key_len": None if w.key_len is None else "per-batch padding",
             "outlier_keys_frac": spec.outlier_frac, "seed": spec.seed,
             "launch_ms_p10": round(per[len(per) // 10], 5),

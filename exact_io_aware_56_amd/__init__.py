@@ -1,8 +1,8 @@
 """Exact IO-aware attention forward for AMD Instinct MI355X (gfx950).
 
-Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` marshal torch
-tensors' device pointers and the current stream into the C entry points of the
-same names; ``fwd`` (and its positional twin ``forward``) additionally
+Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_gqa``
+marshal torch tensors' device pointers and the current stream into the C entry
+points of the same names; ``fwd`` (and its positional twin ``forward``) additionally
 allocates O and LSE. Nothing here computes any part of the attention.
 """
 from __future__ import annotations
@@ -30,13 +30,19 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _check_inputs(q, k, v, o, lse, key_len):
+def _check_inputs(q, k, v, o, lse, key_len, grouped=False):
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors and k, v of one shape")
+    if grouped:
+        B, H, N, d = q.shape
+        if (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d) or H % k.shape[1] != 0:
+            raise ValueError("k, v must be [B, H_kv, N, d] with H_kv dividing q's H")
+    elif k.shape != q.shape:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
     if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPE:
         raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
@@ -78,14 +84,30 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool = False,
                                     _stream(stream)))
 
 
+def fa_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool = False,
+               key_len: Optional[torch.Tensor] = None, q_descale: float = 1.0,
+               k_descale: float = 1.0, v_descale: float = 1.0, stream=None) -> None:
+    """Enqueue fa_fwd_gqa: k, v of shape [B, H_kv, N, d], query head h using
+    K/V head h // (H // H_kv); descales as fa_fwd_fp8, for every dtype."""
+    _check_inputs(q, k, v, o, lse, key_len, grouped=True)
+    B, H, N, d = q.shape
+    _lib._check(_lib.fa_fwd_gqa_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                                    k.shape[1], N, d, scale, causal, _ptr(key_len),
+                                    _DTYPE[q.dtype], q_descale, k_descale, v_descale,
+                                    _stream(stream)))
+
+
 def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
             descale: Tuple[float, float, float] = (1.0, 1.0, 1.0),
             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Allocate O and LSE on q's device and run the forward; returns (O, LSE)."""
+    """Allocate O and LSE on q's device and run the forward; returns (O, LSE).
+    k and v with fewer heads than q take the grouped entry point."""
     B, H, N, d = q.shape
     o = torch.empty((B, H, N, d), dtype=out_dtype(q.dtype), device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if q.dtype == torch.float8_e4m3fn:
+    if k.dim() == 4 and k.shape[1] != H:
+        fa_fwd_gqa(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
+    elif q.dtype == torch.float8_e4m3fn:
         fa_fwd_fp8(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
     else:
         fa_fwd(q, k, v, o, lse, scale, causal, key_len, stream=stream)
@@ -98,7 +120,8 @@ def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
     """softmax(scale * Q K^T + mask) V and its row log-sum-exp, as (O, LSE).
 
     Keyword-only form of ``forward``. q, k, v: contiguous device tensors
-    [B, H, N, d] of one dtype (float32, float16, bfloat16 or float8_e4m3fn);
+    [B, H, N, d] of one dtype (float32, float16, bfloat16 or float8_e4m3fn),
+    or k, v of [B, H_kv, N, d] with H_kv dividing H (grouped K/V heads);
     key_len: optional device int32 [B] of valid key counts. O has q's dtype
     (bfloat16 for fp8 inputs); LSE is float32 [B, H, N], natural log.
     """

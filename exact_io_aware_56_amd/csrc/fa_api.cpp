@@ -24,12 +24,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool positive_finite(float x) { return isfinite(x) && x > 0.0f; }
 
-int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
-            int d, float scale, int causal, const int32_t* key_len, int dtype, float qd, float kd,
-            float vd, void* stream) {
+int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+            int H_kv, int N, int d, float scale, int causal, const int32_t* key_len, int dtype,
+            float qd, float kd, float vd, void* stream) {
   g_last_error[0] = '\0';
   if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N and d must be >= 1");
+  if (H_kv < 1 || H % H_kv != 0) return fail(FA_ERR_INVALID_ARG, "H_kv must be >= 1 and divide H");
   if (dtype < FA_DTYPE_FP32 || dtype > FA_DTYPE_FP8_E4M3)
     return fail(FA_ERR_INVALID_ARG, "dtype is not a fa_dtype value");
   if (!positive_finite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
@@ -58,6 +59,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   p.key_len = key_len;
   p.B = B;
   p.H = H;
+  p.kv_group = H / H_kv;
   p.N = N;
   p.n_qt = (N + rows - 1) / rows;
   const long long grid = (long long)B * H * p.n_qt;
@@ -81,15 +83,22 @@ extern "C" {
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
            int d, float scale, int causal, const int32_t* key_len, int dtype, void* stream) {
-  return forward(Q, K, V, O, LSE, B, H, N, d, scale, causal, key_len, dtype, 1.0f, 1.0f, 1.0f,
+  return forward(Q, K, V, O, LSE, B, H, H, N, d, scale, causal, key_len, dtype, 1.0f, 1.0f, 1.0f,
                  stream);
 }
 
 int fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, void* O_bf16, float* LSE, int B,
                int H, int N, int d, float scale, int causal, const int32_t* key_len,
                float q_descale, float k_descale, float v_descale, void* stream) {
-  return forward(Q8, K8, V8, O_bf16, LSE, B, H, N, d, scale, causal, key_len, FA_DTYPE_FP8_E4M3,
+  return forward(Q8, K8, V8, O_bf16, LSE, B, H, H, N, d, scale, causal, key_len, FA_DTYPE_FP8_E4M3,
                  q_descale, k_descale, v_descale, stream);
+}
+
+int fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+               int H_kv, int N, int d, float scale, int causal, const int32_t* key_len, int dtype,
+               float q_descale, float k_descale, float v_descale, void* stream) {
+  return forward(Q, K, V, O, LSE, B, H, H_kv, N, d, scale, causal, key_len, dtype, q_descale,
+                 k_descale, v_descale, stream);
 }
 
 const char* fa_status_str(int status) {

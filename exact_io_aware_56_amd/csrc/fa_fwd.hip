@@ -192,7 +192,7 @@ __device__ __forceinline__ void map_block(int n_qt, bool causal, int& bh, int& q
 }
 
 struct RowRange {
-  int bh, b, q_wg0, qw0, qrow, kl, nt, wnt, wfull;
+  int bh, kv_bh, b, q_wg0, qw0, qrow, kl, nt, wnt, wfull;
 };
 
 // Which key tiles the workgroup streams (nt) and which of them this wave
@@ -204,6 +204,9 @@ __device__ __forceinline__ RowRange row_range_at(const Params& p, int bh, int qt
                                                  int l32) {
   RowRange r;
   r.bh = bh;
+  // Query heads [g * kv_group, (g + 1) * kv_group) of a batch entry share K/V
+  // head g, so the K/V head of query head bh = b * H + h is bh / kv_group.
+  r.kv_bh = p.kv_group == 1 ? bh : bh / p.kv_group;
   r.b = r.bh / p.H;
   const int N = p.N;
   int kl = N;
@@ -482,9 +485,9 @@ __global__ __launch_bounds__(NW * 64, FA_WAVES_PER_EU) void attn_fwd_16bit(Param
   const int l32 = lane & 31, hi = lane >> 5;
   const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
-  const size_t head = (size_t)rr.bh * N * D;
-  const T* Kh = (const T*)p.k + head;
-  const T* Vh = (const T*)p.v + head;
+  const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;
+  const T* Kh = (const T*)p.k + kv_head;
+  const T* Vh = (const T*)p.v + kv_head;
 
   // Q^T operand: lane holds query row qrow, head-dim 16*s + 8*hi .. +7.
   // Rows at or beyond N read as zeros.
@@ -666,9 +669,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   const int l32 = lane & 31, hi = lane >> 5;
   const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
-  const size_t head = (size_t)rr.bh * N * D;
-  const T* Kh = (const T*)p.k + head;
-  const T* Vh = (const T*)p.v + head;
+  const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;
+  const T* Kh = (const T*)p.k + kv_head;
+  const T* Vh = (const T*)p.v + kv_head;
 
   v8 qf[KS];
   {
@@ -900,10 +903,10 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
     }
   }
   const RowRange rr = row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
-  const size_t head = (size_t)rr.bh * N * D;  // elements
+  const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;  // elements
   const unsigned char* Qh = (const unsigned char*)p.q + head * (KRB / D);
-  const unsigned char* Kh = (const unsigned char*)p.k + head * (KRB / D);
-  const unsigned char* Vh = (const unsigned char*)p.v + head * (KRB / D);
+  const unsigned char* Kh = (const unsigned char*)p.k + kv_head * (KRB / D);
+  const unsigned char* Vh = (const unsigned char*)p.v + kv_head * (KRB / D);
 
   // Q^T operand: lane holds its query row's head-dim elements
   // [16*st + 8*hi, +8) (16-bit) or [64*st + 32*hi, +32) (fp8).
@@ -1224,9 +1227,9 @@ __global__ __launch_bounds__(NW * 64, FA_WAVES_PER_EU) void attn_fwd_fp8(Params 
   const int l32 = lane & 31, hi = lane >> 5;
   const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
-  const size_t head = (size_t)rr.bh * N * D;
-  const T8* Kh = (const T8*)p.k + head;
-  const T8* Vh = (const T8*)p.v + head;
+  const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;
+  const T8* Kh = (const T8*)p.k + kv_head;
+  const T8* Vh = (const T8*)p.v + kv_head;
 
   // Q^T operand: lane holds query row qrow, head-dim 64*s + 32*hi .. +31.
   i32x8 qf[KS];
@@ -1340,9 +1343,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
   const int l32 = lane & 31, hi = lane >> 5;
   const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
-  const size_t head = (size_t)rr.bh * N * D;
-  const float* Kh = (const float*)p.k + head;
-  const float* Vh = (const float*)p.v + head;
+  const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;
+  const float* Kh = (const float*)p.k + kv_head;
+  const float* Vh = (const float*)p.v + kv_head;
 
   // Q^T operand: lane holds Q[qrow][2*s + hi]
   float qf[KS];

@@ -16,6 +16,7 @@ struct Params {
   float* lse;
   const int32_t* key_len;  // NULL: every key valid
   int B, H, N;
+  int kv_group;     // query heads per K/V head (H / H_kv; 1 without grouping)
   int n_qt;         // query tiles per head = ceil(N / rows per workgroup)
   float c;          // scale_eff * log2(e): multiplies raw scores before exp2
   float scale_eff;  // scale * q_descale * k_descale

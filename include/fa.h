@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2  /* 2: fa_fwd_gqa */
 
 typedef enum {
   FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
@@ -58,8 +58,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* a NULL or misaligned pointer, a size < 1, an
                               out-of-range dtype, a scale or descale that is
-                              not finite and > 0, or sizes whose products
-                              overflow                                      */
+                              not finite and > 0, sizes whose products
+                              overflow, or an H_kv that does not divide H   */
   FA_ERR_UNSUPPORTED = -2, /* a head dimension d other than 64 or 128, or
                               one head's N x d tensor of 1 GiB or more      */
   FA_ERR_HIP = -3          /* the HIP runtime refused the launch            */
@@ -100,6 +100,30 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
 int fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, void* O_bf16, float* LSE,
                int B, int H, int N, int d, float scale, int causal,
                const int32_t* key_len, float q_descale, float k_descale,
+               float v_descale, void* stream);
+
+/*
+ * fa_fwd_gqa -- fa_fwd with K/V heads shared by groups of query heads
+ * (multi-query attention, which the FlashAttention-2 paragraph of
+ * FlashAttention (ES), "Evolución y desarrollos posteriores", lists among
+ * that version's additions, and its grouped generalisation).
+ *
+ *   Q, O     as fa_fwd: [B,H,N,d]
+ *   K, V     [in] device, [B,H_kv,N,d] of `dtype`
+ *   H_kv     K/V heads, >= 1 and dividing H. Query head h of a batch entry
+ *            attends with K/V head h / (H / H_kv): consecutive query heads
+ *            form a group. H_kv == 1 is multi-query attention, H_kv == H is
+ *            fa_fwd.
+ *   q_descale, k_descale, v_descale
+ *            as fa_fwd_fp8, for every dtype (1.0 for plain inputs): the
+ *            logits are scale * q_descale * k_descale * (Q K^T) and O is
+ *            v_descale * softmax(...) V.
+ * Other arguments, layouts, masks, ownership and errors as fa_fwd; an H_kv
+ * that is < 1 or does not divide H returns FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int B, int H, int H_kv, int N, int d, float scale, int causal,
+               const int32_t* key_len, int dtype, float q_descale, float k_descale,
                float v_descale, void* stream);
 
 /* A static, human-readable name for a fa_status value (never NULL). */

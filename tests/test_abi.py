@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
     assert _lib.status_name(0) == "FA_OK"
     assert _lib.status_name(-1) == "FA_ERR_INVALID_ARG"
     assert _lib.status_name(-2) == "FA_ERR_UNSUPPORTED"
@@ -79,12 +79,31 @@ def test_fp8_descales_are_validated():
     assert st == -1
 
 
+def gqa_call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=8, H_kv=2, N=16, d=64, scale=0.125, causal=0,
+             key_len=None, dtype=2, qd=1.0, kd=1.0, vd=1.0, stream=None)
+    a.update(kw)
+    return _lib.fa_fwd_gqa_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                               a["H_kv"], a["N"], a["d"], a["scale"], a["causal"], a["key_len"],
+                               a["dtype"], a["qd"], a["kd"], a["vd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=0), -1), (dict(H_kv=-2), -1), (dict(H_kv=3), -1), (dict(H_kv=16), -1),
+    (dict(H=6, H_kv=4), -1), (dict(k=None), -1), (dict(v=P + 8), -1), (dict(qd=0.0), -1),
+    (dict(vd=math.nan), -1), (dict(dtype=5), -1), (dict(d=256), -2), (dict(d=96, H_kv=1), -2),
+])
+def test_grouped_entry_point_rejects_bad_arguments(kw, status):
+    assert gqa_call(**kw) == status
+    assert _lib.load().fa_last_error().decode() != ""
+
+
 def test_python_binding_names_the_entry_points():
     import inspect
 
     import exact_io_aware_56_amd as fa
 
-    assert callable(fa.fa_fwd) and callable(fa.fa_fwd_fp8)
+    assert callable(fa.fa_fwd) and callable(fa.fa_fwd_fp8) and callable(fa.fa_fwd_gqa)
     sig = inspect.signature(fa.fwd)
     assert list(sig.parameters)[:3] == ["q", "k", "v"]
     for name in ("scale", "causal", "key_len"):

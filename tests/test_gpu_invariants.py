@@ -105,3 +105,24 @@ def test_outputs_untouched_on_argument_error():
         fa.fa_fwd(q, k, v, o, lse, -1.0)
     torch.cuda.synchronize()
     assert torch.all(o == 7.0) and torch.all(lse == 7.0)
+
+
+@pytest.mark.parametrize("dtype,N,causal", [("bf16", 300, True), ("fp16", 4200, True),
+                                            ("fp8", 4096, False), ("fp32", 129, False)])
+def test_grouped_heads_equal_repeated_heads_bit_for_bit(dtype, N, causal):
+    """fa_fwd_gqa on [B,H_kv,N,d] K/V equals fa_fwd on the same K/V heads
+    repeated to H: the same arithmetic on the same values, only addressed
+    differently."""
+    d = 128 if dtype == "fp8" else 64
+    H, H_kv = 8, 2
+    w = draw_small("decoder_causal_bf16", B=1, H=H, N=N, d=d, dtype=dtype, causal=causal,
+                   seed=95, H_kv=H_kv)
+    say(f"case grouped == repeated dtype={dtype} N={N} causal={causal}")
+    q, k, v, _ = to_device(w)
+    o_g, lse_g = fa.forward(q, k, v, 0.125, causal, None, descale=w.descale)
+    rep = H // H_kv
+    k_r = w.k.repeat_interleave(rep, dim=1).contiguous().to(DEV)
+    v_r = w.v.repeat_interleave(rep, dim=1).contiguous().to(DEV)
+    o_r, lse_r = fa.forward(q, k_r, v_r, 0.125, causal, None, descale=w.descale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r) and torch.equal(lse_g, lse_r)

@@ -164,7 +164,7 @@ def test_named_workload_full_oracle(name):
     assert_close(o, lse, o_ref, lse_ref, w.spec.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["long_causal_bf16", "long_causal_fp8"])
+@pytest.mark.parametrize("name", ["long_causal_bf16", "long_causal_fp8", "long_causal_grouped_bf16"])
 def test_named_workload_sampled_rows(name):
     """Full-size long-context workloads: every head, sampled rows (tile edges,
     the outlier keys' own rows, random rows) against the oracle row by row."""
@@ -177,7 +177,8 @@ def test_named_workload_sampled_rows(name):
     errs_o, errs_l = [], []
     for b in range(s.B):
         for h in range(s.H):
-            extra = None if w.outlier_rows is None else w.outlier_rows[b, h][:8]
+            g = h // (s.H // s.kv_heads)
+            extra = None if w.outlier_rows is None else w.outlier_rows[b, g][:8]
             rows = sampled_rows(s, rng, per_head=24, extra=extra)
             o_ref, lse_ref = oracle.attention_rows(q, k, v, s.scale, s.causal,
                                                    w.key_len_or_none(), b, h, rows)
@@ -191,3 +192,28 @@ def test_named_workload_sampled_rows(name):
         f"max|dLSE|={el.max():.3e}")
     assert np.all(np.isfinite(o))
     assert eo.max() <= t["max_o"] and eo.mean() <= t["mean_o"] and el.max() <= t["lse"]
+
+
+# Grouped K/V heads (fa_fwd_gqa): every kernel family, multi-query (H_kv = 1),
+# grouped and ungrouped through the grouped entry point, both masks.
+GROUPED = [  # dtype, d, N, causal, padded, H, H_kv
+    ("bf16", 64, 300, True, False, 8, 2), ("bf16", 128, 129, False, True, 6, 3),
+    ("fp16", 128, 257, True, True, 4, 1), ("fp16", 64, 65, False, False, 4, 4),
+    ("fp32", 64, 200, True, True, 6, 2), ("fp32", 128, 33, False, False, 3, 1),
+    ("fp8", 128, 300, True, False, 8, 2), ("fp8", 64, 127, False, True, 4, 1),
+    # sequences long enough for the pipelined kernel
+    ("bf16", 128, 4161, True, False, 4, 1), ("fp16", 64, 4096, False, True, 4, 2),
+    ("fp8", 128, 4160, True, True, 2, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,d,N,causal,padded,H,H_kv", GROUPED)
+def test_grouped_kv_heads(dtype, d, N, causal, padded, H, H_kv):
+    spec = small_spec(dtype, d, N, causal, padded, B=2 if N < 1000 else 1, H=H,
+                      seed=9500 + N + H_kv).with_shape(H_kv=H_kv)
+    say(f"case grouped dtype={dtype} d={d} N={N} causal={causal} padded={padded} "
+        f"H={H} H_kv={H_kv} seed={spec.seed}")
+    w = W.draw(spec)
+    o, lse = run(w)
+    o_ref, lse_ref = full_oracle(w)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"H={H} H_kv={H_kv}")

@@ -73,3 +73,14 @@ def test_oracle_fixture_does_not_drift():
         fin = np.isfinite(ref_l)
         assert np.array_equal(np.isfinite(lse.reshape(-1)), fin)
         assert np.abs(lse.reshape(-1)[fin] - ref_l[fin]).max() <= 1e-14
+
+
+def test_grouped_workload_shapes():
+    s = small("long_causal_grouped_bf16", H=8, H_kv=2, N=100, d=8)
+    w = W.draw(s)
+    assert tuple(w.q.shape) == (1, 8, 100, 8)
+    assert tuple(w.k.shape) == (1, 2, 100, 8) and tuple(w.v.shape) == (1, 2, 100, 8)
+    assert w.outlier_rows.shape == (1, 2, 1)
+    # an ungrouped spec of the same seed draws the same Q
+    u = W.draw(s.with_shape(H_kv=None))
+    assert torch.equal(w.q, u.q)

@@ -7,10 +7,11 @@ and the CPU oracle can consume its output without sharing any of the method.
 Recipe (the same for every workload):
 
 * ``numpy.random.default_rng(seed)`` (PCG64); draw ``standard_normal`` in
-  float64 in the order Q, K, V, each of shape ``[B, H, N, d]``, then cast each
-  to float32.
-* Outlier keys (the long-context decoder workload): for every (b, h), in that
-  order, ``rng.choice(N, round(frac * N), replace=False)`` picks distinct key
+  float64 in the order Q, K, V, Q of shape ``[B, H, N, d]`` and K, V of shape
+  ``[B, H_kv, N, d]`` (H_kv = H unless the workload groups K/V heads), then
+  cast each to float32.
+* Outlier keys (the long-context decoder workloads): for every (b, K/V head),
+  in that order, ``rng.choice(N, round(frac * N), replace=False)`` picks distinct key
   rows that are multiplied by ``outlier_scale`` (in float32, exact).
 * Key padding: ``key_len[b] = rng.integers(lo, hi + 1)`` for each batch entry,
   drawn after the outliers; shared by all heads of that batch entry.
@@ -57,6 +58,11 @@ class Spec:
     outlier_frac: float = 0.0
     outlier_scale: float = 8.0
     seed: int = 0
+    H_kv: Optional[int] = None  # K/V heads (None: H, no grouping)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.H_kv is None else self.H_kv
 
     def flops(self) -> float:
         """Nominal attention FLOP: 4*B*H*N^2*d, halved when causal."""
@@ -84,6 +90,11 @@ SPECS = {
                              1.0 / math.sqrt(128), outlier_frac=0.01, seed=20260004),
     "long_causal_fp8": Spec("long_causal_fp8", 1, 32, 16384, 128, "fp8", True,
                             1.0 / math.sqrt(128), seed=20260005),
+    # The long causal decoder shape with 8 K/V heads, each shared by 4 query
+    # heads (grouped multi-query attention).
+    "long_causal_grouped_bf16": Spec("long_causal_grouped_bf16", 1, 32, 8192, 128, "bf16", True,
+                                     1.0 / math.sqrt(128), outlier_frac=0.01, seed=20260006,
+                                     H_kv=8),
 }
 ORDER = list(SPECS)
 
@@ -96,7 +107,7 @@ class Workload:
     v: torch.Tensor
     key_len: Optional[np.ndarray]  # int32 [B] or None
     descale: Tuple[float, float, float]  # (q, k, v); 1.0 unless fp8
-    outlier_rows: Optional[np.ndarray] = None  # int64 [B,H,n_out]
+    outlier_rows: Optional[np.ndarray] = None  # int64 [B,H_kv,n_out]
 
     def exact(self):
         """float64 arrays (q, k, v) holding exactly the values the storage represents."""
@@ -123,15 +134,16 @@ def draw(spec: Spec, seed: Optional[int] = None) -> Workload:
     """Generate the workload for ``spec`` (seed defaults to the spec's own)."""
     rng = np.random.default_rng(spec.seed if seed is None else seed)
     shape = (spec.B, spec.H, spec.N, spec.d)
+    kv_shape = (spec.B, spec.kv_heads, spec.N, spec.d)
     q = rng.standard_normal(shape).astype(np.float32)
-    k = rng.standard_normal(shape).astype(np.float32)
-    v = rng.standard_normal(shape).astype(np.float32)
+    k = rng.standard_normal(kv_shape).astype(np.float32)
+    v = rng.standard_normal(kv_shape).astype(np.float32)
     rows = None
     if spec.outlier_frac > 0:
         n_out = int(round(spec.outlier_frac * spec.N))
-        rows = np.zeros((spec.B, spec.H, n_out), dtype=np.int64)
+        rows = np.zeros((spec.B, spec.kv_heads, n_out), dtype=np.int64)
         for b in range(spec.B):
-            for h in range(spec.H):
+            for h in range(spec.kv_heads):
                 idx = rng.choice(spec.N, n_out, replace=False)
                 rows[b, h] = idx
                 k[b, h, idx, :] *= np.float32(spec.outlier_scale)
