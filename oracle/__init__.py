@@ -12,6 +12,7 @@ Every function here is pinned by tests that do not reuse its own formulas
 (arbitrary-precision brute force, a second library's attention routine,
 closed forms and invariants); none is "parity unpinned".
 """
-from .attention import (attention_forward, attention_rows, probabilities,  # noqa: F401
+from .attention import (attention_forward, attention_rows, attention_decode,  # noqa: F401
+                        probabilities,
                         masked_scores, softmax_stats, allowed_mask, clamp_key_len)
 from .online import online_forward  # noqa: F401

@@ -125,6 +125,43 @@ def attention_rows(q, k, v, scale: float, causal: bool, key_len, b: int, h: int,
                          causal, kl)
 
 
+def attention_decode(q, k, v, scale: float, causal: bool = False,
+                     key_len: Optional[Sequence[int]] = None):
+    """O [B,H,Nq,d] and LSE [B,H,Nq] (float64) for the newest Nq queries of each
+    batch entry against its key/value cache: q [B,H,Nq,d], k, v [B,H_kv,Nk,d].
+
+    FlashAttention (ES), "Soluciones especializadas", names attention over the
+    KV cache of streaming generation (FlashInfer) as a use of the method, and
+    its bibliography lists FlashDecoding++; neither is defined there. Reading:
+    batch entry b holds kl_b = clamp(key_len[b], 0, Nk) valid keys (Nk when
+    key_len is None), and its Nq queries are the last Nq positions of that
+    sequence, so query i sits at position kl_b - Nq + i. Key j is allowed iff
+    j < kl_b and, when causal, j <= kl_b - Nq + i. With Nq = Nk and every key
+    valid this is attention_forward's mask; a query with no allowed key gets
+    O = 0 and LSE = -inf. K/V heads are grouped as in attention_forward.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    o = np.zeros((B, H, Nq, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    i = np.arange(Nq)
+    j = np.arange(Nk)
+    for b in range(B):
+        kl = clamp_key_len(key_len, b, Nk)
+        ok = np.broadcast_to(j[None, :] < kl, (Nq, Nk))
+        if causal:
+            ok = ok & (j[None, :] <= (kl - Nq + i)[:, None])
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            s = np.where(ok, float(scale) * (q[b, h] @ k[b, g].T), -np.inf)
+            p, m, l = softmax_stats(s)
+            o[b, h] = p @ v[b, g]
+            with np.errstate(divide="ignore"):
+                lse[b, h] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return o, lse
+
+
 def probabilities(q, k, scale: float, causal: bool, key_len, b: int, h: int):
     """The full N x N probability matrix P of one (b, h), for checks on P itself."""
     N = q.shape[2]

@@ -380,3 +380,108 @@ def test_multi_query_with_equal_query_heads_gives_equal_outputs():
         lse_close(L[0, h], L1[0, 0], 0.0)
     with pytest.raises(ValueError):
         oracle.attention_forward(q, np.zeros((1, 3, 24, 8)), np.zeros((1, 3, 24, 8)), 0.4, False)
+
+
+# ---------------------------------------------------------------------------
+# Decode: the newest Nq queries against a key/value cache of kl_b valid keys
+
+def brute_force_decode(q, k, v, scale, causal, key_len):
+    """Decode definition written out with no max subtraction, 50 digits."""
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    O = np.zeros((B, H, Nq, d))
+    L = np.zeros((B, H, Nq))
+    for b in range(B):
+        kl = Nk if key_len is None else min(max(int(key_len[b]), 0), Nk)
+        for h in range(H):
+            g = h // (H // H_kv)
+            for i in range(Nq):
+                pos = kl - Nq + i
+                allowed = [j for j in range(Nk) if j < kl and (not causal or j <= pos)]
+                if not allowed:
+                    L[b, h, i] = -np.inf
+                    continue
+                w = {j: mpmath.exp(mpmath.mpf(scale) * mpmath.fsum(
+                    mpmath.mpf(float(q[b, h, i, t])) * mpmath.mpf(float(k[b, g, j, t]))
+                    for t in range(d))) for j in allowed}
+                z = mpmath.fsum(w.values())
+                for t in range(d):
+                    O[b, h, i, t] = float(mpmath.fsum(w[j] * mpmath.mpf(float(v[b, g, j, t]))
+                                                      for j in allowed) / z)
+                L[b, h, i] = float(mpmath.log(z))
+    return O, L
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_matches_brute_force(causal):
+    rng = np.random.default_rng(611 + causal)
+    B, H, H_kv, Nq, Nk, d = 3, 4, 2, 3, 11, 4
+    q = rng.standard_normal((B, H, Nq, d))
+    k = rng.standard_normal((B, H_kv, Nk, d))
+    v = rng.standard_normal((B, H_kv, Nk, d))
+    key_len = np.array([11, 5, 2])  # the last entry leaves query 0 no key when causal
+    O, L = oracle.attention_decode(q, k, v, 0.6, causal, key_len)
+    O2, L2 = brute_force_decode(q, k, v, 0.6, causal, key_len)
+    assert np.abs(O - O2).max() <= 1e-13
+    lse_close(L, L2, 1e-13)
+    if causal:
+        assert np.all(O[2, :, 0] == 0.0) and np.all(L[2, :, 0] == -np.inf)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_with_every_position_is_the_forward(causal):
+    rng = np.random.default_rng(44)
+    q, k, v = rand_qkv(rng, 2, 3, 29, 8)
+    O, L = oracle.attention_decode(q, k, v, 0.3, causal)
+    O2, L2 = oracle.attention_forward(q, k, v, 0.3, causal)
+    assert np.abs(O - O2).max() == 0.0
+    lse_close(L, L2, 0.0)
+
+
+def test_decode_rows_are_the_causal_forward_rows_at_their_positions():
+    # Place the Nq decode queries at positions kl-Nq .. kl-1 of a full query
+    # sequence over the first kl keys: the causal forward's rows there are the
+    # decode outputs.
+    rng = np.random.default_rng(45)
+    B, H, Nq, Nk, d = 2, 2, 4, 30, 8
+    q = rng.standard_normal((B, H, Nq, d))
+    k = rng.standard_normal((B, H, Nk, d))
+    v = rng.standard_normal((B, H, Nk, d))
+    key_len = np.array([30, 17])
+    O, L = oracle.attention_decode(q, k, v, 0.4, True, key_len)
+    for b, kl in enumerate(key_len):
+        qf = rng.standard_normal((1, H, kl, d))
+        qf[0, :, kl - Nq:] = q[b]
+        Of, Lf = oracle.attention_forward(qf, k[b:b + 1, :, :kl], v[b:b + 1, :, :kl], 0.4, True)
+        assert np.abs(O[b] - Of[0, :, kl - Nq:]).max() <= 1e-14
+        lse_close(L[b], Lf[0, :, kl - Nq:], 1e-14)
+
+
+def test_decode_matches_torch_sdpa_bottom_right_mask():
+    rng = np.random.default_rng(46)
+    B, H, H_kv, Nq, Nk, d = 3, 6, 3, 5, 40, 16
+    q = rng.standard_normal((B, H, Nq, d))
+    k = rng.standard_normal((B, H_kv, Nk, d))
+    v = rng.standard_normal((B, H_kv, Nk, d))
+    key_len = np.array([40, 23, 9])
+    O, _ = oracle.attention_decode(q, k, v, 0.25, True, key_len)
+    j = torch.arange(Nk)
+    i = torch.arange(Nq)
+    kl = torch.as_tensor(key_len)
+    mask = (j[None, None, :] < kl[:, None, None]) & (
+        j[None, None, :] <= (kl[:, None, None] - Nq + i[None, :, None]))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask[:, None],
+        scale=0.25, enable_gqa=True)
+    assert np.abs(O - ref.numpy()).max() <= 1e-12
+
+
+def test_single_query_decode_sees_every_valid_key():
+    rng = np.random.default_rng(47)
+    q = rng.standard_normal((2, 2, 1, 8))
+    k = rng.standard_normal((2, 2, 25, 8))
+    v = rng.standard_normal((2, 2, 25, 8))
+    key_len = np.array([25, 7])
+    a = oracle.attention_decode(q, k, v, 0.5, True, key_len)
+    b = oracle.attention_decode(q, k, v, 0.5, False, key_len)
+    assert np.abs(a[0] - b[0]).max() == 0.0
