@@ -60,6 +60,15 @@ def measured_traffic(workload: str):
     return float(val.group(1))
 
 
+def decode_bytes(spec, key_len) -> int:
+    """Decode: each batch entry's valid K/V rows read once, Q read once, O and
+    LSE written once."""
+    e = {"fp16": 2, "bf16": 2}[spec.dtype]
+    kl = spec.N * spec.B if key_len is None else int(key_len.sum())
+    qo = 2 * e * spec.B * spec.H * spec.Nq * spec.d
+    return 2 * e * spec.kv_heads * spec.d * kl + qo + 4 * spec.B * spec.H * spec.Nq
+
+
 def algorithmic_bytes(spec) -> int:
     """Q, K, V read once, O written once, LSE written once (K and V have
     H_kv heads when the workload groups them)."""
@@ -84,6 +93,20 @@ def cpu_baseline(w, budget_s: float):
     s = w.spec
     q, k, v = w.exact()
     kl = w.key_len_or_none()
+    if s.is_decode:
+        done = 0
+        t0 = time.perf_counter()
+        for b in range(s.B):
+            oracle.attention_decode(q[b:b + 1], k[b:b + 1], v[b:b + 1], s.scale, s.causal,
+                                    None if kl is None else kl[b:b + 1])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": round(s.flops() / s.B * done / dt / 1e12, 6), "unit": "TFLOP/s",
+                "cores": int(threads), "kind": "oracle",
+                "sample": f"{done} of {s.B} sequences of the same workload, every head, "
+                          f"float64, {dt:.2f} s wall"}
     heads = 0
     t0 = time.perf_counter()
     for b in range(s.B):
@@ -154,9 +177,15 @@ def main(argv=None):
     o = torch.empty(q.shape, dtype=fa.out_dtype(q.dtype), device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    ws = None
+    if spec.is_decode:
+        nbytes = fa.decode_workspace_bytes(spec.B, spec.H, spec.kv_heads, spec.Nq, spec.N, spec.d)
+        ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
     def step():
-        if spec.kv_heads != spec.H:
+        if spec.is_decode:
+            fa.fa_fwd_decode(q, k, v, o, lse, ws, spec.scale, spec.causal, kl, stream=stream)
+        elif spec.kv_heads != spec.H:
             fa.fa_fwd_gqa(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
         elif spec.dtype == "fp8":
             fa.fa_fwd_fp8(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
@@ -206,6 +235,16 @@ def main(argv=None):
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     traffic = measured_traffic(spec.name) if default_n else None
     exps = spec.exps()
+    if spec.is_decode:
+        # HBM-bound: the roofline is bytes moved, the two kernels of a step
+        # (split pass and merge) timed together
+        alg = decode_bytes(spec, w.key_len)
+        gbs = alg / (avg_launch_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                    "frac": round(gbs / 8000.0, 4), "traffic": traffic, "algorithmic_bytes": alg,
+                    "kernel_sources_sha256_16": kernel_sha()}
+    else:
+        roofline = None
     result = {
         "metric": METRIC if spec.name == "long_causal_bf16" and default_n else
         f"attention fwd TFLOP/s ({spec.name}, N={spec.N})",
@@ -224,7 +263,7 @@ def main(argv=None):
         "config": {
             "workload": spec.name, "B": spec.B, "H": spec.H, "N": spec.N, "d": spec.d,
             "causal": spec.causal, "scale": spec.scale,
-            "H_kv": spec.kv_heads,
+            "H_kv": spec.kv_heads, "Nq": spec.q_len,
             "key_len": None if w.key_len is None else "per-batch padding",
             "outlier_keys_frac": spec.outlier_frac, "seed": spec.seed,
             "launch_ms_p10": round(per[len(per) // 10], 5),
@@ -232,7 +271,7 @@ def main(argv=None):
             "launch_ms_p90": round(per[(9 * len(per)) // 10], 5),
             "host_wall_s": round(wall, 4),
         },
-        "roofline": {
+        "roofline": roofline or {
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": peak,
@@ -248,7 +287,7 @@ def main(argv=None):
                     "frac": round(exps / (avg_launch_ms * 1e-3) / 1e12 / EXP_PEAK_T, 4)},
         },
     }
-    if w.key_len is not None and not spec.causal:
+    if w.key_len is not None and (not spec.causal or spec.is_decode):
         eff = spec.flops() * float(w.key_len.sum()) / (spec.B * spec.N)
         result["config"]["effective_tflops"] = round(eff / (ms_per_step * 1e-3) / 1e12, 3)
     if args.cpu_budget > 0:

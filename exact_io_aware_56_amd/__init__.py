@@ -1,8 +1,8 @@
 """Exact IO-aware attention forward for AMD Instinct MI355X (gfx950).
 
-Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_gqa``
-marshal torch tensors' device pointers and the current stream into the C entry
-points of the same names; ``fwd`` (and its positional twin ``forward``) additionally
+Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_gqa`` /
+``fa_fwd_decode`` marshal torch tensors' device pointers and the current stream
+into the C entry points of the same names; ``fwd`` (and its positional twin ``forward``) additionally
 allocates O and LSE. Nothing here computes any part of the attention.
 """
 from __future__ import annotations
@@ -12,7 +12,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import FaError, abi_version, load, status_name  # noqa: F401
+from ._lib import FaError, abi_version, decode_workspace_bytes, load, status_name  # noqa: F401
 
 _DTYPE = {
     torch.float32: _lib.FA_DTYPE_FP32,
@@ -126,3 +126,48 @@ def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
     (bfloat16 for fp8 inputs); LSE is float32 [B, H, N], natural log.
     """
     return forward(q, k, v, scale, causal, key_len, descale, stream)
+
+
+def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool = False,
+                  key_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue fa_fwd_decode: q [B, H, Nq, d], k, v [B, H_kv, Nk, d] (16-bit),
+    o like q, lse float32 [B, H, Nq], workspace a contiguous device tensor of at
+    least decode_workspace_bytes(...) bytes."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse),
+                    ("workspace", workspace)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q [B, H, Nq, d] and k, v [B, H_kv, Nk, d] expected")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d or H % k.shape[1] != 0:
+        raise ValueError("k, v must be [B, H_kv, Nk, d] with H_kv dividing H")
+    if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must be [B, H, Nq, d] of q's dtype")
+    if lse.shape != q.shape[:3] or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Nq]")
+    if key_len is not None and (not key_len.is_cuda or key_len.dtype != torch.int32
+                                or key_len.shape != (B,) or not key_len.is_contiguous()):
+        raise ValueError("key_len must be a contiguous device int32 tensor of shape [B]")
+    nbytes = workspace.numel() * workspace.element_size()
+    _lib._check(_lib.fa_fwd_decode_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                                       k.shape[1], Nq, k.shape[2], d, scale, causal,
+                                       _ptr(key_len), _DTYPE[q.dtype], _ptr(workspace), nbytes,
+                                       _stream(stream)))
+
+
+def decode(q, k, v, *, scale: float, causal: bool = False, key_len=None,
+           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode against a key/value cache, allocating O, LSE and the workspace;
+    returns (O, LSE). See fa_fwd_decode for the layouts and the mask."""
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = decode_workspace_bytes(B, H, k.shape[1], Nq, k.shape[2], d)
+    if nbytes == 0:
+        raise ValueError("invalid decode sizes")
+    ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    fa_fwd_decode(q, k, v, o, lse, ws, scale, causal, key_len, stream=stream)
+    return o, lse

@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_status_str", "fa_abi_version",
-            "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_decode", "fa_decode_workspace_bytes",
+            "fa_status_str", "fa_abi_version", "fa_last_error")
 
 _lib = None
 
@@ -42,6 +42,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_fp8.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, f, f, f, vp]
     lib.fa_fwd_gqa.restype = i
+    sz = ctypes.c_size_t
+    lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_fwd_decode.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -81,3 +86,14 @@ def fa_fwd_gqa_raw(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, dt
                    stream) -> int:
     return load().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, float(scale), int(causal),
                              key_len, int(dtype), float(qd), float(kd), float(vd), stream)
+
+
+def decode_workspace_bytes(B, H, H_kv, Nq, Nk, d) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d))
+
+
+def fa_fwd_decode_raw(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, key_len, dtype,
+                      workspace, workspace_bytes, stream) -> int:
+    return load().fa_fwd_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, float(scale),
+                                int(causal), key_len, int(dtype), workspace,
+                                int(workspace_bytes), stream)

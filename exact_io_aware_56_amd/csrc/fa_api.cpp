@@ -5,6 +5,7 @@
 // keeps no state besides a per-thread description of the last error.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 
@@ -77,6 +78,94 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   return FA_OK;
 }
 
+// Rows per K/V head, 32-row blocks, key chunks and tiles per chunk of a
+// decode call, and the workspace bytes it needs; false if the sizes are out
+// of range.
+struct DecodeShape {
+  int R, n_rb, S, chunk_tiles;
+  long long units, ws_bytes;
+};
+
+bool decode_shape(int B, int H, int H_kv, int Nq, int Nk, int d, DecodeShape& sh) {
+  if (B < 1 || H < 1 || H_kv < 1 || Nq < 1 || Nk < 1 || d < 1 || H % H_kv != 0) return false;
+  const long long R = (long long)(H / H_kv) * Nq;
+  if (R > 0x7fffffffLL - 31) return false;
+  sh.R = (int)R;
+  sh.n_rb = (int)((R + 31) / 32);
+  const long long base = (long long)B * H_kv * sh.n_rb;
+  if (base > 0x7fffffffLL) return false;
+  sh.S = fa::decode_splits((int)base, Nk, &sh.chunk_tiles);
+  sh.units = base * sh.S;
+  const __int128 rows = (__int128)B * H * Nq;
+  const __int128 bytes = rows * sh.S * (d + 1) * 4 + 256;
+  if (sh.units > 0x7fffffffLL || rows > 0x7fffffff || bytes > (__int128)INT64_MAX) return false;
+  sh.ws_bytes = (long long)bytes;
+  return true;
+}
+
+int decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+           int H_kv, int Nq, int Nk, int d, float scale, int causal, const int32_t* key_len,
+           int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H, Nq, Nk and d must be >= 1");
+  if (H_kv < 1 || H % H_kv != 0) return fail(FA_ERR_INVALID_ARG, "H_kv must be >= 1 and divide H");
+  if (dtype < FA_DTYPE_FP32 || dtype > FA_DTYPE_FP8_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "dtype is not a fa_dtype value");
+  if (!positive_finite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(workspace, 16))
+    return fail(FA_ERR_INVALID_ARG, "Q, K, V, O and the workspace must be 16-byte aligned");
+  if (!aligned(LSE, 4) || (key_len && !aligned(key_len, 4)))
+    return fail(FA_ERR_INVALID_ARG, "LSE and key_len must be 4-byte aligned");
+  if ((__int128)B * H * Nq * d * 4 > (__int128)INT64_MAX ||
+      (__int128)B * H_kv * Nk * d * 4 > (__int128)INT64_MAX)
+    return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  DecodeShape sh;
+  if (!decode_shape(B, H, H_kv, Nq, Nk, d, sh)) return fail(FA_ERR_INVALID_ARG, "sizes out of range");
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16)
+    return fail(FA_ERR_UNSUPPORTED, "decode takes bfloat16 or float16 inputs");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if ((long long)Nk * d * 2 >= (1LL << 30))
+    return fail(FA_ERR_UNSUPPORTED, "one head's Nk x d tensor must be under 1 GiB");
+  if ((long long)workspace_bytes < sh.ws_bytes)
+    return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_decode_workspace_bytes()");
+
+  fa::DecodeParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.key_len = key_len;
+  const long long rows = (long long)B * H * Nq;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = p.ws_o + rows * sh.S * d;
+  p.B = B;
+  p.H = H;
+  p.H_kv = H_kv;
+  p.group = H / H_kv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.R = sh.R;
+  p.n_rb = sh.n_rb;
+  p.S = sh.S;
+  p.chunk_tiles = sh.chunk_tiles;
+  p.units = (int)sh.units;
+  p.scale_eff = scale;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.o_scale = 1.0f;
+  const hipError_t e = fa::launch_decode(static_cast<fa::Kind>(dtype), d, causal != 0, p,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,6 +188,20 @@ int fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
                float q_descale, float k_descale, float v_descale, void* stream) {
   return forward(Q, K, V, O, LSE, B, H, H_kv, N, d, scale, causal, key_len, dtype, q_descale,
                  k_descale, v_descale, stream);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d) {
+  DecodeShape sh;
+  if (!decode_shape(B, H, H_kv, Nq, Nk, d, sh)) return 0;
+  return (size_t)sh.ws_bytes;
+}
+
+int fa_fwd_decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                  int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                  const int32_t* key_len, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return decode(Q, K, V, O, LSE, B, H, H_kv, Nq, Nk, d, scale, causal, key_len, dtype, workspace,
+                workspace_bytes, stream);
 }
 
 const char* fa_status_str(int status) {

@@ -32,6 +32,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -41,6 +42,7 @@ namespace fa {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -1453,6 +1455,159 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_f32(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode against a key/value cache: few queries, long key sequences
+//
+// Split over keys: every wave owns one (K/V head, 32-row block, key chunk)
+// unit, where the rows are the group's query heads times the Nq queries
+// (row r: query head g * group + r / Nq, query r % Nq) and the chunk is a run
+// of 32-key tiles. It streams its tiles once from HBM (K straight into the
+// MFMA operand registers, V through a private LDS slice for the transposing
+// reads), keeps the online softmax of its rows, and writes the normalised
+// partial O and its LSE to the workspace. attn_decode_merge then combines a
+// row's chunks: LSE = log sum exp(LSE_s), O = sum exp(LSE_s - LSE) O_s. The
+// waves of a workgroup share nothing, so a wave without a unit just exits.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeWaves = 4;
+
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kDecodeWaves * 64, 2) void attn_decode_split(DecodeParams p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16;            // S MFMA steps over the head dim
+  constexpr int DB = D / 32;            // 32-wide head-dim blocks of O^T
+  constexpr int RB = D * 2;             // bytes per K / V row
+  constexpr int VST = D + FA_V_SKEW;    // V row stride in LDS (elements)
+  constexpr int CPR = D / 8;            // 16-byte pieces per row
+  constexpr int VCH = 32 * CPR / 64;    // V pieces per lane per 32-key tile
+  __shared__ __attribute__((aligned(16))) T vs[kDecodeWaves][32 * VST];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * kDecodeWaves + wave;
+  if (unit >= p.units) return;
+  const int chunk = unit % p.S;
+  const int rest = unit / p.S;
+  const int rb = rest % p.n_rb;
+  const int kvh = rest / p.n_rb;  // b * H_kv + g
+  const int b = kvh / p.H_kv, g = kvh - b * p.H_kv;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int r = rb * 32 + l32;
+  const bool row_ok = r < p.R;
+  const int hq = g * p.group + (row_ok ? r / p.Nq : 0);
+  const int qi = row_ok ? r % p.Nq : 0;
+  const size_t qrow = ((size_t)b * p.H + hq) * p.Nq + qi;  // row of Q, O and LSE
+
+  int kl = p.Nk;
+  if (p.key_len != nullptr) {
+    const int x = p.key_len[b];
+    kl = x < 0 ? 0 : (x > p.Nk ? p.Nk : x);
+  }
+  kl = __builtin_amdgcn_readfirstlane(kl);
+  const int nt = (kl + 31) / 32;
+  const int t0 = chunk * p.chunk_tiles;
+  const int t1 = min(nt, t0 + p.chunk_tiles);
+  const int pos = kl - p.Nq + qi;  // the query's position: causal keys j <= pos
+
+  // Q^T operand: lane holds its row's head-dim elements [16*st + 8*hi, +8).
+  v8 qf[KS];
+  {
+    const T* qr = (const T*)p.q + qrow * D;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qf[st] = row_ok ? *(const v8*)(qr + 16 * st + 8 * hi) : v8{};
+  }
+  // K / V of the K/V head over its first kl rows: rows beyond read as zeros.
+  const size_t kv_off = (size_t)kvh * p.Nk * RB;
+  const auto rsK = buffer_rsrc((const unsigned char*)p.k + kv_off, kl * RB);
+  const auto rsV = buffer_rsrc((const unsigned char*)p.v + kv_off, kl * RB);
+  i32x4 kr[KS], vr[VCH];
+  auto load = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < KS; ++st) kr[st] = load16(rsK, (32 * t + l32) * RB + 32 * st + 16 * hi);
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int pc = lane + 64 * c;
+      vr[c] = load16(rsV, (32 * t + pc / CPR) * RB + 16 * (pc % CPR));
+    }
+  };
+  T* vt = vs[wave];
+
+  const float c = p.c;
+  const float thr = fminf(kRescaleLog2 / c, 1e30f);
+  float m = -INFINITY, l = 0.0f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+
+  if (t0 < t1) load(t0);
+  for (int t = t0; t < t1; ++t) {
+    f32x16 sc[1] = {f32x16{}};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) sc[0] = E::mma(__builtin_bit_cast(v8, kr[st]), qf[st], sc[0]);
+    // V of tile t into this wave's slice; the previous tile's reads of it
+    // were issued earlier by this wave, and LDS serves a wave in order.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int cc = 0; cc < VCH; ++cc) {
+      const int pc = lane + 64 * cc;
+      *(i32x4*)(vt + (pc / CPR) * VST + 8 * (pc % CPR)) = vr[cc];
+    }
+    if (t + 1 < t1) load(t + 1);
+    if (CAUSAL || 32 * (t + 1) > kl) apply_mask<1, CAUSAL>(sc, 32 * t, kl, pos, hi);
+    v8 pf[2];
+    online_softmax<E, 1, DB>(sc, c, thr, m, l, o, pf);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the V slice is written
+    __builtin_amdgcn_wave_barrier();
+    pv_product<E, 1, DB, VST>(vt, lane, pf, o);
+  }
+
+  const float lt = sum_halves(l);
+  const bool live = lt > 0.0f;
+  const float inv = live ? 1.0f / lt : 0.0f;
+  if (row_ok) {
+    float* wo = p.ws_o + (qrow * p.S + chunk) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = o[db][4 * gq + e] * inv;
+        *(f32x4*)(wo + 32 * db + 8 * gq + 4 * hi) = x;
+      }
+    if (hi == 0) p.ws_lse[qrow * p.S + chunk] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
+  }
+}
+
+// One wave per query row: combine its S partial results.
+template <class OutT, int D>
+__global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
+  constexpr int E = D / 64;  // head-dim elements per lane
+  const size_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* ls = p.ws_lse + row * p.S;
+  float mx = -INFINITY;
+  for (int s = lane; s < p.S; s += 64) mx = fmaxf(mx, ls[s]);
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) mx = fmaxf(mx, __shfl_xor(mx, w, 64));
+  float acc[E] = {};
+  float L = 0.0f;
+  if (mx > -INFINITY) {
+    const float* wo = p.ws_o + row * p.S * D;
+    for (int s = 0; s < p.S; ++s) {
+      const float w = expf(ls[s] - mx);  // 0 for an empty chunk
+      L += w;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(w, wo[(size_t)s * D + lane + 64 * e], acc[e]);
+    }
+  }
+  const float inv = L > 0.0f ? p.o_scale / L : 0.0f;
+  OutT* out = (OutT*)p.o + row * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[lane + 64 * e] = (OutT)(acc[e] * inv);
+  if (lane == 0) p.lse[row] = L > 0.0f ? mx + logf(L) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // Launch table
 // ---------------------------------------------------------------------------
 constexpr int kWaves = FA_WAVES;  // x 32 query rows per workgroup
@@ -1528,6 +1683,45 @@ int rows_per_block(Kind kind, int d, int N, bool causal) {
 hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream) {
   if (d == 64) return causal ? launch_d<64, true>(kind, p, stream) : launch_d<64, false>(kind, p, stream);
   if (d == 128) return causal ? launch_d<128, true>(kind, p, stream) : launch_d<128, false>(kind, p, stream);
+  return hipErrorInvalidValue;
+}
+
+int decode_splits(int units_base, int Nk, int* chunk_tiles) {
+  // About 8 waves per CU in all, chunks of at least four 32-key tiles.
+  const int nt = (Nk + 31) / 32;
+  const long long target = 2048;
+  long long S = (target + units_base - 1) / units_base;
+  S = std::max(1LL, std::min(S, (long long)(nt + 3) / 4));
+  const int ct = (int)((nt + S - 1) / S);
+  *chunk_tiles = ct;
+  return (nt + ct - 1) / ct;
+}
+
+namespace {
+template <class E, int D, bool C>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+  DecodeParams local = p;
+  void* args[] = {&local};
+  const long long grid = ((long long)p.units + kDecodeWaves - 1) / kDecodeWaves;
+  const long long rows = (long long)p.B * p.H * p.Nq;
+  if (grid <= 0 || grid > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipError_t e = hipLaunchKernel((const void*)attn_decode_split<E, D, C>, dim3((unsigned)grid),
+                                 dim3(kDecodeWaves * 64), args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)attn_decode_merge<typename E::T, D>, dim3((unsigned)rows),
+                         dim3(64), args, 0, stream);
+}
+template <class E>
+hipError_t launch_decode_e(int d, bool causal, const DecodeParams& p, hipStream_t s) {
+  if (d == 64) return causal ? launch_decode_t<E, 64, true>(p, s) : launch_decode_t<E, 64, false>(p, s);
+  if (d == 128) return causal ? launch_decode_t<E, 128, true>(p, s) : launch_decode_t<E, 128, false>(p, s);
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_decode(Kind kind, int d, bool causal, const DecodeParams& p, hipStream_t stream) {
+  if (kind == Kind::BF16) return launch_decode_e<Bf16>(d, causal, p, stream);
+  if (kind == Kind::F16) return launch_decode_e<F16>(d, causal, p, stream);
   return hipErrorInvalidValue;
 }
 

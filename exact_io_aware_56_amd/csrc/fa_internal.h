@@ -23,6 +23,25 @@ struct Params {
   float o_scale;    // v_descale
 };
 
+// Decode (few queries against a key/value cache), split over keys.
+struct DecodeParams {
+  const void* q;  // [B, H, Nq, D]
+  const void* k;  // [B, H_kv, Nk, D]
+  const void* v;
+  void* o;        // [B, H, Nq, D]
+  float* lse;     // [B, H, Nq]
+  const int32_t* key_len;
+  float* ws_o;    // workspace: [B*H*Nq][S][D] normalised partial O
+  float* ws_lse;  // workspace: [B*H*Nq][S] partial LSE
+  int B, H, H_kv, group, Nq, Nk;
+  int R;            // rows per K/V head: group * Nq
+  int n_rb;         // 32-row blocks per K/V head
+  int S;            // key chunks
+  int chunk_tiles;  // 32-key tiles per chunk
+  int units;        // B * H_kv * n_rb * S waves of work
+  float c, scale_eff, o_scale;
+};
+
 enum class Kind { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 
 // Rows of Q owned by one workgroup for a problem's kind, d, N and mask; 0 if
@@ -32,5 +51,13 @@ int rows_per_block(Kind kind, int d, int N, bool causal);
 // Enqueue the forward on `stream`. Arguments are already validated and
 // p.n_qt filled in. Returns the launch's hipError_t.
 hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream);
+
+// Key chunks S (and 32-key tiles per chunk) for `units_base` = B*H_kv*n_rb
+// (K/V head, row block) pairs over Nk keys. Deterministic in its arguments:
+// the workspace size and the launch both use it.
+int decode_splits(int units_base, int Nk, int* chunk_tiles);
+
+// Enqueue the split pass and the merge on `stream` (16-bit kinds only).
+hipError_t launch_decode(Kind kind, int d, bool causal, const DecodeParams& p, hipStream_t stream);
 
 }  // namespace fa

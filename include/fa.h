@@ -39,13 +39,14 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2  /* 2: fa_fwd_gqa */
+#define FA_ABI_VERSION 3  /* 2: fa_fwd_gqa; 3: fa_fwd_decode */
 
 typedef enum {
   FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
@@ -125,6 +126,48 @@ int fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int H, int H_kv, int N, int d, float scale, int causal,
                const int32_t* key_len, int dtype, float q_descale, float k_descale,
                float v_descale, void* stream);
+
+/*
+ * fa_fwd_decode -- the newest Nq queries of each batch entry against its
+ * key/value cache (attention over the KV cache of streaming generation, which
+ * FlashAttention (ES), "Soluciones especializadas", names as a use of the
+ * method; FlashDecoding++ in its bibliography).
+ *
+ *   Q        [in]  device, [B,H,Nq,d] of `dtype`
+ *   K, V     [in]  device, [B,H_kv,Nk,d] of `dtype` (the caches)
+ *   O        [out] device, [B,H,Nq,d] of `dtype`
+ *   LSE      [out] device, float [B,H,Nq], natural log
+ *   H_kv     K/V heads, >= 1 and dividing H, grouped as in fa_fwd_gqa
+ *   Nq, Nk   queries per head and cache length, each >= 1
+ *   key_len  NULL or device int32 [B]: batch entry b holds kl_b =
+ *            clamp(key_len[b], 0, Nk) valid keys (Nk when NULL)
+ *   causal   query i sits at position kl_b - Nq + i: key j is allowed iff
+ *            j < kl_b and, when causal, j <= kl_b - Nq + i. A query with no
+ *            allowed key gets O = 0 and LSE = -inf.
+ *   dtype    FA_DTYPE_BF16 or FA_DTYPE_FP16 (others: FA_ERR_UNSUPPORTED)
+ *   workspace, workspace_bytes
+ *            device scratch owned by the caller, 16-byte aligned, at least
+ *            fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d) bytes; its
+ *            contents on entry do not matter and on return are undefined.
+ *            Calls that overlap in time need separate workspaces.
+ *   d, scale, stream as fa_fwd.
+ *
+ * The keys of each K/V head are split into chunks processed in parallel,
+ * each writing a normalised partial O and its LSE to the workspace; a second
+ * kernel on the same stream merges a row's chunks. Errors as fa_fwd, plus
+ * FA_ERR_INVALID_ARG for a NULL, misaligned or too small workspace.
+ */
+int fa_fwd_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                  const int32_t* key_len, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * Workspace bytes fa_fwd_decode needs for these sizes (it depends on nothing
+ * else); 0 if the sizes are invalid (a value < 1, H_kv not dividing H, or
+ * products out of range).
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
 
 /* A static, human-readable name for a fa_status value (never NULL). */
 const char* fa_status_str(int status);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
     assert _lib.status_name(0) == "FA_OK"
     assert _lib.status_name(-1) == "FA_ERR_INVALID_ARG"
     assert _lib.status_name(-2) == "FA_ERR_UNSUPPORTED"
@@ -96,6 +96,39 @@ def gqa_call(**kw):
 def test_grouped_entry_point_rejects_bad_arguments(kw, status):
     assert gqa_call(**kw) == status
     assert _lib.load().fa_last_error().decode() != ""
+
+
+def decode_call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=8, H_kv=2, Nq=1, Nk=4096, d=128, scale=0.1,
+             causal=1, key_len=None, dtype=2, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return _lib.fa_fwd_decode_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                  a["H_kv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                  a["key_len"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), -1), (dict(ws=P + 8), -1), (dict(ws_bytes=1024), -1), (dict(q=None), -1),
+    (dict(Nq=0), -1), (dict(Nk=0), -1), (dict(H_kv=3), -1), (dict(H_kv=0), -1),
+    (dict(scale=math.nan), -1), (dict(dtype=7), -1), (dict(lse=P + 1), -1),
+    (dict(dtype=0), -2), (dict(dtype=3), -2), (dict(d=256), -2), (dict(Nk=1 << 22), -2),
+])
+def test_decode_entry_point_rejects_bad_arguments(kw, status):
+    assert decode_call(**kw) == status
+    assert _lib.load().fa_last_error().decode() != ""
+
+
+def test_decode_workspace_size():
+    ws = _lib.decode_workspace_bytes
+    n = ws(2, 8, 2, 1, 4096, 128)
+    assert n > 0 and n % 4 == 0
+    # exactly too small is rejected before anything is enqueued
+    assert decode_call(ws_bytes=n - 1) == -1
+    assert ws(2, 8, 3, 1, 4096, 128) == 0 and ws(0, 8, 2, 1, 64, 64) == 0
+    assert ws(1, 1, 1, 1, 1, 64) > 0
+    # covers one partial O row and LSE per (query row, chunk)
+    rows = 2 * 8 * 1
+    assert n >= rows * 4 * (128 + 1)
 
 
 def test_python_binding_names_the_entry_points():

@@ -7,8 +7,9 @@ and the CPU oracle can consume its output without sharing any of the method.
 Recipe (the same for every workload):
 
 * ``numpy.random.default_rng(seed)`` (PCG64); draw ``standard_normal`` in
-  float64 in the order Q, K, V, Q of shape ``[B, H, N, d]`` and K, V of shape
-  ``[B, H_kv, N, d]`` (H_kv = H unless the workload groups K/V heads), then
+  float64 in the order Q, K, V, Q of shape ``[B, H, Nq, d]`` and K, V of shape
+  ``[B, H_kv, N, d]`` (H_kv = H unless the workload groups K/V heads; Nq = N
+  except for decode workloads, whose Nq queries meet a cache of N keys), then
   cast each to float32.
 * Outlier keys (the long-context decoder workloads): for every (b, K/V head),
   in that order, ``rng.choice(N, round(frac * N), replace=False)`` picks distinct key
@@ -59,18 +60,32 @@ class Spec:
     outlier_scale: float = 8.0
     seed: int = 0
     H_kv: Optional[int] = None  # K/V heads (None: H, no grouping)
+    Nq: Optional[int] = None    # decode: queries per head against N cached keys
+
+    @property
+    def is_decode(self) -> bool:
+        return self.Nq is not None
+
+    @property
+    def q_len(self) -> int:
+        return self.N if self.Nq is None else self.Nq
 
     @property
     def kv_heads(self) -> int:
         return self.H if self.H_kv is None else self.H_kv
 
     def flops(self) -> float:
-        """Nominal attention FLOP: 4*B*H*N^2*d, halved when causal."""
+        """Nominal attention FLOP: 4*B*H*N^2*d, halved when causal; decode:
+        4*B*H*Nq*N*d (every query against the whole cache)."""
+        if self.is_decode:
+            return 4.0 * self.B * self.H * self.Nq * self.N * self.d
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
     def exps(self) -> float:
         """Nominal exponentials (one per score): B*H*N^2, halved when causal."""
+        if self.is_decode:
+            return float(self.B) * self.H * self.Nq * self.N
         e = float(self.B) * self.H * self.N * self.N
         return e / 2 if self.causal else e
 
@@ -95,6 +110,11 @@ SPECS = {
     "long_causal_grouped_bf16": Spec("long_causal_grouped_bf16", 1, 32, 8192, 128, "bf16", True,
                                      1.0 / math.sqrt(128), outlier_frac=0.01, seed=20260006,
                                      H_kv=8),
+    # One new token per sequence against a 16K-key cache: 16 sequences whose
+    # caches hold 8K..16K valid keys, 32 query heads over 8 K/V heads.
+    "decode_grouped_bf16": Spec("decode_grouped_bf16", 16, 32, 16384, 128, "bf16", True,
+                                1.0 / math.sqrt(128), key_len_range=(8192, 16384),
+                                seed=20260007, H_kv=8, Nq=1),
 }
 ORDER = list(SPECS)
 
@@ -133,7 +153,7 @@ def _quantise_fp8(x: np.ndarray):
 def draw(spec: Spec, seed: Optional[int] = None) -> Workload:
     """Generate the workload for ``spec`` (seed defaults to the spec's own)."""
     rng = np.random.default_rng(spec.seed if seed is None else seed)
-    shape = (spec.B, spec.H, spec.N, spec.d)
+    shape = (spec.B, spec.H, spec.q_len, spec.d)
     kv_shape = (spec.B, spec.kv_heads, spec.N, spec.d)
     q = rng.standard_normal(shape).astype(np.float32)
     k = rng.standard_normal(kv_shape).astype(np.float32)
