@@ -16,3 +16,4 @@ from .attention import (attention_forward, attention_rows, attention_decode,  # 
                         probabilities,
                         masked_scores, softmax_stats, allowed_mask, clamp_key_len)
 from .online import online_forward  # noqa: F401
+from .backward import attention_backward  # noqa: F401
