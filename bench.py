@@ -78,6 +78,45 @@ def algorithmic_bytes(spec) -> int:
     return ((e_in + e_out) * spec.H + 2 * e_in * spec.kv_heads) * row + 4 * spec.B * spec.H * spec.N
 
 
+def cpu_baseline_backward(w, budget_s: float):
+    """The float64 backward oracle on whole heads until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    s = w.spec
+    q, k, v = w.exact()
+    rng = np.random.default_rng(s.seed + 1)
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(s.B):
+        for h in range(s.H):
+            g = h // (s.H // s.kv_heads)
+            do = rng.standard_normal((1, 1, s.N, s.d))
+            oracle.attention_backward(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1],
+                                      v[b:b + 1, g:g + 1], do, s.scale, s.causal,
+                                      None if w.key_len is None else w.key_len[b:b + 1])
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 2.5 * s.flops() / (s.B * s.H) * heads
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{heads} of {s.B * s.H} heads of the same workload's backward, every "
+                      f"query row, float64, {dt:.2f} s wall"}
+
+
+def _threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i["num_threads"] for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the float64 oracle on whole heads of the workload until the budget
     is spent (at least one head); returns the JSON object."""
@@ -134,6 +173,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="long_causal_bf16")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dQ, dK, dV) of the workload instead of the "
+                         "forward; FLOP counted as 2.5x the forward's (five N^2 d products)")
     ap.add_argument("--N", type=int, default=0,
                     help="override the workload's sequence length (HBM scaling runs); "
                          "such a line is not the headline measurement")
@@ -182,8 +224,23 @@ def main(argv=None):
         nbytes = fa.decode_workspace_bytes(spec.B, spec.H, spec.kv_heads, spec.Nq, spec.N, spec.d)
         ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
+    if args.backward:
+        if spec.is_decode or spec.dtype not in ("bf16", "fp16"):
+            print(json.dumps({"error": "the backward covers 16-bit forward workloads"}))
+            return 2
+        o_f, lse_f = fa.fwd(q, k, v, scale=spec.scale, causal=spec.causal, key_len=kl)
+        g = torch.Generator(device="cpu").manual_seed(spec.seed + 1)
+        dout = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+        grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        ws = torch.empty((fa.bwd_workspace_bytes(spec.B, spec.H, spec.N) + 15) // 16 * 4,
+                         dtype=torch.float32, device=dev)
+        o = grads[0]
+
     def step():
-        if spec.is_decode:
+        if args.backward:
+            fa.fa_bwd(q, k, v, o_f, dout, lse_f, *grads, ws, spec.scale, spec.causal, kl,
+                      stream=stream)
+        elif spec.is_decode:
             fa.fa_fwd_decode(q, k, v, o, lse, ws, spec.scale, spec.causal, kl, stream=stream)
         elif spec.kv_heads != spec.H:
             fa.fa_fwd_gqa(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
@@ -229,11 +286,11 @@ def main(argv=None):
     avg_launch_ms = sum(per) / len(per)
     ms_per_step = total_ms / args.steps
 
-    flop = spec.flops()
+    flop = spec.flops() * (2.5 if args.backward else 1.0)
     value = flop / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[spec.dtype]
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
-    traffic = measured_traffic(spec.name) if default_n else None
+    traffic = measured_traffic(spec.name) if default_n and not args.backward else None
     exps = spec.exps()
     if spec.is_decode:
         # HBM-bound: the roofline is bytes moved, the two kernels of a step
@@ -246,8 +303,8 @@ def main(argv=None):
     else:
         roofline = None
     result = {
-        "metric": METRIC if spec.name == "long_causal_bf16" and default_n else
-        f"attention fwd TFLOP/s ({spec.name}, N={spec.N})",
+        "metric": METRIC if spec.name == "long_causal_bf16" and default_n and not args.backward
+        else f"attention {'bwd' if args.backward else 'fwd'} TFLOP/s ({spec.name}, N={spec.N})",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -290,8 +347,12 @@ def main(argv=None):
     if w.key_len is not None and (not spec.causal or spec.is_decode):
         eff = spec.flops() * float(w.key_len.sum()) / (spec.B * spec.N)
         result["config"]["effective_tflops"] = round(eff / (ms_per_step * 1e-3) / 1e12, 3)
+    if args.backward:
+        result["config"]["pass"] = "backward"
+        result["roofline"]["exp"] = None
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = (cpu_baseline_backward if args.backward else cpu_baseline)(
+            w, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
 

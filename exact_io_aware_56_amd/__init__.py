@@ -1,7 +1,7 @@
 """Exact IO-aware attention forward for AMD Instinct MI355X (gfx950).
 
 Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_gqa`` /
-``fa_fwd_decode`` marshal torch tensors' device pointers and the current stream
+``fa_fwd_decode`` / ``fa_bwd`` marshal torch tensors' device pointers and the current stream
 into the C entry points of the same names; ``fwd`` (and its positional twin ``forward``) additionally
 allocates O and LSE. Nothing here computes any part of the attention.
 """
@@ -12,7 +12,8 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import FaError, abi_version, decode_workspace_bytes, load, status_name  # noqa: F401
+from ._lib import (FaError, abi_version, bwd_workspace_bytes, decode_workspace_bytes,  # noqa: F401
+                   load, status_name)
 
 _DTYPE = {
     torch.float32: _lib.FA_DTYPE_FP32,
@@ -171,3 +172,46 @@ def decode(q, k, v, *, scale: float, causal: bool = False, key_len=None,
     ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=q.device)
     fa_fwd_decode(q, k, v, o, lse, ws, scale, causal, key_len, stream=stream)
     return o, lse
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal: bool = False,
+           key_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue fa_bwd: q, o, do, dq [B, H, N, d]; k, v, dk, dv [B, H_kv, N, d]
+    (16-bit); lse float32 [B, H, N]; workspace of bwd_workspace_bytes(B, H, N)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse),
+                    ("dq", dq), ("dk", dk), ("dv", dv), ("workspace", workspace)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, H, N, d = q.shape
+    if k.dim() != 4 or (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d) or H % k.shape[1]:
+        raise ValueError("k, v must be [B, H_kv, N, d] with H_kv dividing H")
+    for name, t, shape in (("v", v, k.shape), ("o", o, q.shape), ("do", do, q.shape),
+                           ("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
+        if t.shape != shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have shape {tuple(shape)} and q's dtype")
+    if q.dtype not in (torch.bfloat16, torch.float16) or k.dtype != q.dtype:
+        raise ValueError("the backward takes bfloat16 or float16 tensors")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    if key_len is not None and (not key_len.is_cuda or key_len.dtype != torch.int32
+                                or key_len.shape != (B,) or not key_len.is_contiguous()):
+        raise ValueError("key_len must be a contiguous device int32 tensor of shape [B]")
+    nbytes = workspace.numel() * workspace.element_size()
+    _lib._check(_lib.fa_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                _ptr(dk), _ptr(dv), B, H, k.shape[1], N, d, scale, causal,
+                                _ptr(key_len), _DTYPE[q.dtype], _ptr(workspace), nbytes,
+                                _stream(stream)))
+
+
+def bwd(q, k, v, o, lse, do, *, scale: float, causal: bool = False, key_len=None,
+        stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dQ, dK, dV) of the forward that returned (o, lse) for these
+    inputs, given the upstream gradient do; allocates outputs and workspace."""
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    nbytes = bwd_workspace_bytes(B, H, N)
+    ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale, causal, key_len, stream=stream)
+    return dq, dk, dv

@@ -16,7 +16,8 @@ FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_decode", "fa_decode_workspace_bytes",
-            "fa_status_str", "fa_abi_version", "fa_last_error")
+            "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version",
+            "fa_last_error")
 
 _lib = None
 
@@ -47,6 +48,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_decode.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -97,3 +102,13 @@ def fa_fwd_decode_raw(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, key
     return load().fa_fwd_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, float(scale),
                                 int(causal), key_len, int(dtype), workspace,
                                 int(workspace_bytes), stream)
+
+
+def bwd_workspace_bytes(B, H, N) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, N))
+
+
+def fa_bwd_raw(q, k, v, o, do, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, key_len, dtype,
+               workspace, workspace_bytes, stream) -> int:
+    return load().fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, H_kv, N, d, float(scale),
+                         int(causal), key_len, int(dtype), workspace, int(workspace_bytes), stream)

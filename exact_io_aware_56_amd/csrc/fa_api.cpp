@@ -166,6 +166,73 @@ int decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   return FA_OK;
 }
 
+long long bwd_workspace(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  const __int128 rows = (__int128)B * H * N;
+  if (rows * 8 + 256 > (__int128)INT64_MAX) return 0;
+  return (long long)(rows * 8 + 256);
+}
+
+int backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int H_kv, int N, int d,
+             float scale, int causal, const int32_t* key_len, int dtype, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+  if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N and d must be >= 1");
+  if (H_kv < 1 || H % H_kv != 0) return fail(FA_ERR_INVALID_ARG, "H_kv must be >= 1 and divide H");
+  if (dtype < FA_DTYPE_FP32 || dtype > FA_DTYPE_FP8_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "dtype is not a fa_dtype value");
+  if (!positive_finite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const void* al16[] = {Q, K, V, O, dO, dQ, dK, dV, workspace};
+  for (const void* x : al16)
+    if (!aligned(x, 16)) return fail(FA_ERR_INVALID_ARG, "tensors and the workspace must be 16-byte aligned");
+  if (!aligned(LSE, 4) || (key_len && !aligned(key_len, 4)))
+    return fail(FA_ERR_INVALID_ARG, "LSE and key_len must be 4-byte aligned");
+  if ((__int128)B * H * N * d * 4 > (__int128)INT64_MAX) return fail(FA_ERR_INVALID_ARG, "B*H*N*d overflows");
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16)
+    return fail(FA_ERR_UNSUPPORTED, "the backward takes bfloat16 or float16 tensors");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if ((long long)N * d * 2 >= (1LL << 30)) return fail(FA_ERR_UNSUPPORTED, "one head's N x d tensor must be under 1 GiB");
+  const long long need = bwd_workspace(B, H, N);
+  if (need == 0 || (long long)workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_bwd_workspace_bytes()");
+  const long long tiles = (N + 127) / 128;
+  if ((long long)B * H * tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "grid too large");
+
+  fa::BwdParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.lse = LSE;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.key_len = key_len;
+  p.delta = static_cast<float*>(workspace);
+  p.lse2 = p.delta + (long long)B * H * N;
+  p.B = B;
+  p.H = H;
+  p.H_kv = H_kv;
+  p.group = H / H_kv;
+  p.N = N;
+  p.n_qt = (int)tiles;
+  p.n_kt = (int)tiles;
+  p.scale = scale;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  const hipError_t e = fa::launch_backward(static_cast<fa::Kind>(dtype), d, causal != 0, p,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +269,16 @@ int fa_fwd_decode(const void* Q, const void* K, const void* V, void* O, float* L
                   void* stream) {
   return decode(Q, K, V, O, LSE, B, H, H_kv, Nq, Nk, d, scale, causal, key_len, dtype, workspace,
                 workspace_bytes, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) { return (size_t)bwd_workspace(B, H, N); }
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int H_kv, int N, int d,
+           float scale, int causal, const int32_t* key_len, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H_kv, N, d, scale, causal, key_len, dtype,
+                  workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_str(int status) {

@@ -1608,6 +1608,314 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Backward: dQ, dK, dV by recomputing P from the forward's LSE
+//
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),  Delta = rowsum(dO * O),
+//   dQ = scale * dS K,  dK = scale * dS^T Q,  P = exp2(c*s - LSE*log2(e)).
+// Three passes on one stream: attn_bwd_prep writes Delta and LSE*log2(e) per
+// query row; attn_bwd_dq gives every wave 32 query rows and streams the
+// 32-key K/V tiles (the forward's orientation: lanes own queries, so LSE and
+// Delta are per-lane values); attn_bwd_dkdv gives every wave 32 keys and
+// streams 32-query Q/dO tiles over the query heads that share its K/V head
+// (lanes own keys, so dK and dV accumulate with no cross-wave reduction and
+// no atomics). Both recompute S; products whose second operand comes out of
+// an accumulator (dQ from dS^T, dV from P, dK from dS) use pv_product, the
+// forward's transposing-read product.
+// ---------------------------------------------------------------------------
+constexpr int kBwdWaves = 4;               // waves per workgroup
+constexpr int kBwdRows = kBwdWaves * 32;   // query rows (dQ) or keys (dK/dV) per workgroup
+constexpr int kBwdSkew = 32;               // extra 16-bit elements per LDS row
+
+// Delta and LSE * log2(e) of every query row: D/8 lanes per row, 16 bytes each.
+template <class T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep(BwdParams p) {
+  typedef T v8t __attribute__((ext_vector_type(8)));
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const long long rows = (long long)p.B * p.H * p.N;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const v8t a = *(const v8t*)((const T*)p.dout + row * D + 8 * part);
+    const v8t b = *(const v8t*)((const T*)p.o + row * D + 8 * part);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+  }
+#pragma unroll
+  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 64);
+  if (row < rows && part == 0) {
+    p.delta[row] = acc;
+    const float L = p.lse[row];
+    p.lse2[row] = L == -INFINITY ? INFINITY : L * 1.4426950408889634f;
+  }
+}
+
+// The row's 16 accumulator values scaled and written as 4-element runs: lane
+// owns column `col` of the D-layout tile, rows are the head-dim elements.
+template <class T, int DB>
+__device__ __forceinline__ void store_grad(T* row_ptr, int hi, float scale, const f32x16 (&a)[DB]) {
+  typedef T v4t __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      v4t out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (T)(a[db][4 * g + e] * scale);
+      *(v4t*)(row_ptr + 32 * db + 8 * g + 4 * hi) = out;
+    }
+}
+
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq(BwdParams p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, ST = D + kBwdSkew;
+  constexpr int NT = kBwdWaves * 64;
+  constexpr int CH = (32 * CPR + NT - 1) / NT;  // 16-byte pieces per thread per tile
+  static_assert(32 * CPR % NT == 0, "tile pieces split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) T ks[2][32 * ST];
+  __shared__ __attribute__((aligned(16))) T vs[2][32 * ST];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int N = p.N;
+  const int bh = blockIdx.x / p.n_qt;
+  const int qt = p.n_qt - 1 - (blockIdx.x - bh * p.n_qt);  // longest causal tiles first
+  const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
+  int kl = N;
+  if (p.key_len != nullptr) {
+    const int x = p.key_len[b];
+    kl = x < 0 ? 0 : (x > N ? N : x);
+  }
+  kl = __builtin_amdgcn_readfirstlane(kl);
+  const int q_wg0 = qt * kBwdRows, qw0 = q_wg0 + 32 * wave, qrow = qw0 + l32;
+  int kv_end = kl;
+  if (CAUSAL) kv_end = min(kv_end, min(N, q_wg0 + kBwdRows));
+  const int nt = (kv_end + 31) / 32;
+  int w_end = CAUSAL ? min(kv_end, qw0 + 32) : kv_end;
+  if (qw0 >= N) w_end = 0;
+  const int wnt = (w_end + 31) / 32;
+  int wfull = kl / 32;
+  if (CAUSAL) wfull = min(wfull, (qw0 + 1) / 32);
+  wfull = min(wfull, wnt);
+
+  const size_t head = (size_t)bh * N * D, kv_head = (size_t)kvh * N * D;
+  const T* Kh = (const T*)p.k + kv_head;
+  const T* Vh = (const T*)p.v + kv_head;
+  v8 qf[KS], df[KS];
+  {
+    const auto rq = tile_rsrc((const T*)p.q + head, 0, N, N, D * 2);
+    const auto rd = tile_rsrc((const T*)p.dout + head, 0, N, N, D * 2);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      qf[st] = __builtin_bit_cast(v8, load16(rq, qrow * D * 2 + 32 * st + 16 * hi));
+      df[st] = __builtin_bit_cast(v8, load16(rd, qrow * D * 2 + 32 * st + 16 * hi));
+    }
+  }
+  const bool row_ok = qrow < N;
+  const float lse2 = row_ok ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
+  const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.0f;
+  const float c = p.c;
+
+  i32x4 kreg[CH], vreg[CH];
+  auto gload = [&](int j) __attribute__((always_inline)) {
+    const auto rk = tile_rsrc(Kh, j, 32, kv_end, D * 2);
+    const auto rv = tile_rsrc(Vh, j, 32, kv_end, D * 2);
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const int piece = tid + cc * NT;
+      const int off = ((piece / CPR) * D + (piece % CPR) * 8) * 2;
+      kreg[cc] = load16(rk, off);
+      vreg[cc] = load16(rv, off);
+    }
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const int piece = tid + cc * NT;
+      const int r = piece / CPR, col = (piece % CPR) * 8;
+      *(i32x4*)(&ks[buf][r * ST + col]) = kreg[cc];
+      *(i32x4*)(&vs[buf][r * ST + col]) = vreg[cc];
+    }
+  };
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const int buf = j & 1;
+    gload(j + 1);
+    auto tile = [&](auto masked) __attribute__((always_inline)) {
+      f32x16 s[1] = {f32x16{}};
+      f32x16 dp = {};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const v8 a = *(const v8*)(ks[buf] + l32 * ST + 16 * st + 8 * hi);
+        s[0] = E::mma(a, qf[st], s[0]);
+        const v8 bv = *(const v8*)(vs[buf] + l32 * ST + 16 * st + 8 * hi);
+        dp = E::mma(bv, df[st], dp);
+      }
+      if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
+      v8 ds[2];
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * ps + e;
+          const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
+          ds[ps][e] = E::cvt(pr * (dp[i] - dl));
+        }
+      pv_product<E, 1, DB, ST>(ks[buf], lane, ds, dq);
+    };
+    if (j < wfull) tile(std::false_type{});
+    else if (j < wnt) tile(std::true_type{});
+    sstore(buf ^ 1);
+    __syncthreads();
+  }
+  if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
+}
+
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dkdv(BwdParams p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, ST = D + kBwdSkew;
+  constexpr int NT = kBwdWaves * 64;
+  constexpr int CH = (32 * CPR + NT - 1) / NT;
+  static_assert(32 * CPR % NT == 0, "tile pieces split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) T qs[2][32 * ST];
+  __shared__ __attribute__((aligned(16))) T dos[2][32 * ST];
+  __shared__ __attribute__((aligned(16))) float ls[2][32];
+  __shared__ __attribute__((aligned(16))) float dls[2][32];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int N = p.N;
+  const int kvh = blockIdx.x / p.n_kt;
+  const int kt = blockIdx.x - kvh * p.n_kt;
+  const int b = kvh / p.H_kv, g = kvh - b * p.H_kv;
+  int kl = N;
+  if (p.key_len != nullptr) {
+    const int x = p.key_len[b];
+    kl = x < 0 ? 0 : (x > N ? N : x);
+  }
+  kl = __builtin_amdgcn_readfirstlane(kl);
+  const int k_wg0 = kt * kBwdRows, kw0 = k_wg0 + 32 * wave, key = kw0 + l32;
+  // Query tiles [t_begin, nqt) of every query head in the group; none if the
+  // workgroup's keys are all padding.
+  const int nqt = (N + 31) / 32;
+  const int t_begin = CAUSAL ? k_wg0 / 32 : 0;
+  const int per_head = k_wg0 < kl ? nqt - t_begin : 0;
+  const int n_iter = per_head * p.group;
+  const bool wave_live = kw0 < kl;
+
+  const size_t kv_head = (size_t)kvh * N * D;
+  v8 kf[KS], vf[KS];
+  {
+    const auto rk = tile_rsrc((const T*)p.k + kv_head, 0, N, N, D * 2);
+    const auto rv = tile_rsrc((const T*)p.v + kv_head, 0, N, N, D * 2);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      kf[st] = __builtin_bit_cast(v8, load16(rk, key * D * 2 + 32 * st + 16 * hi));
+      vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
+    }
+  }
+  const float c = p.c;
+
+  i32x4 qreg[CH], dreg[CH];
+  float lreg = INFINITY, dlreg = 0.0f;
+  auto gload = [&](int u) __attribute__((always_inline)) {
+    const int hq = g * p.group + (per_head > 0 ? u / max(per_head, 1) : 0);
+    const int t = t_begin + (per_head > 0 ? u % max(per_head, 1) : 0);
+    const size_t qhead = ((size_t)b * p.H + hq) * N;
+    const bool any = u < n_iter;
+    const auto rq = tile_rsrc((const T*)p.q + qhead * D, t, 32, any ? N : 0, D * 2);
+    const auto rd = tile_rsrc((const T*)p.dout + qhead * D, t, 32, any ? N : 0, D * 2);
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const int piece = tid + cc * NT;
+      const int off = ((piece / CPR) * D + (piece % CPR) * 8) * 2;
+      qreg[cc] = load16(rq, off);
+      dreg[cc] = load16(rd, off);
+    }
+    if (tid < 32) {
+      const int row = 32 * t + tid;
+      const bool ok = any && row < N;
+      lreg = ok ? p.lse2[qhead + row] : INFINITY;
+      dlreg = ok ? p.delta[qhead + row] : 0.0f;
+    }
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const int piece = tid + cc * NT;
+      const int r = piece / CPR, col = (piece % CPR) * 8;
+      *(i32x4*)(&qs[buf][r * ST + col]) = qreg[cc];
+      *(i32x4*)(&dos[buf][r * ST + col]) = dreg[cc];
+    }
+    if (tid < 32) {
+      ls[buf][tid] = lreg;
+      dls[buf][tid] = dlreg;
+    }
+  };
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dk[db] = f32x16{}, dv[db] = f32x16{};
+  if (n_iter > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int u = 0; u < n_iter; ++u) {
+    const int buf = u & 1;
+    const int t = t_begin + u % per_head;
+    gload(u + 1);
+    // this wave's keys see some query of the tile
+    if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const v8 a = *(const v8*)(qs[buf] + l32 * ST + 16 * st + 8 * hi);
+        s = E::mma(a, kf[st], s);
+        const v8 d = *(const v8*)(dos[buf] + l32 * ST + 16 * st + 8 * hi);
+        dp = E::mma(d, vf[st], dp);
+      }
+      // element i is query 32t + r(i), r(i) = 8*(i/4) + 4*hi + i%4, key `key`
+      v8 pf[2], dsf[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *(const f32x4*)(&ls[buf][8 * q4 + 4 * hi]);
+        const f32x4 d4 = *(const f32x4*)(&dls[buf][8 * q4 + 4 * hi]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          const int qry = 32 * t + 8 * q4 + 4 * hi + e;
+          const bool ok = key < kl && (!CAUSAL || key <= qry);
+          const float pr = ok ? fast_exp2(fmaf(s[i], c, -l4[e])) : 0.0f;
+          pf[i >> 3][i & 7] = E::cvt(pr);
+          dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
+        }
+      }
+      pv_product<E, 1, DB, ST>(dos[buf], lane, pf, dv);
+      pv_product<E, 1, DB, ST>(qs[buf], lane, dsf, dk);
+    }
+    sstore(buf ^ 1);
+    __syncthreads();
+  }
+  if (key < N) {
+    store_grad<T, DB>((T*)p.dk + kv_head + (size_t)key * D, hi, p.scale, dk);
+    store_grad<T, DB>((T*)p.dv + kv_head + (size_t)key * D, hi, 1.0f, dv);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch table
 // ---------------------------------------------------------------------------
 constexpr int kWaves = FA_WAVES;  // x 32 query rows per workgroup
@@ -1718,6 +2026,40 @@ hipError_t launch_decode_e(int d, bool causal, const DecodeParams& p, hipStream_
   return hipErrorInvalidValue;
 }
 }  // namespace
+
+namespace {
+template <class E, int D, bool C>
+hipError_t launch_backward_t(const BwdParams& p, hipStream_t stream) {
+  BwdParams local = p;
+  void* args[] = {&local};
+  const long long rows = (long long)p.B * p.H * p.N;
+  const long long g_prep = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
+  const long long g_dq = (long long)p.B * p.H * p.n_qt;
+  const long long g_kv = (long long)p.B * p.H_kv * p.n_kt;
+  if (g_prep > 0x7fffffffLL || g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
+  hipError_t e = hipLaunchKernel((const void*)attn_bwd_prep<typename E::T, D>, dim3((unsigned)g_prep),
+                                 dim3(256), args, 0, stream);
+  if (e != hipSuccess) return e;
+  e = hipLaunchKernel((const void*)attn_bwd_dq<E, D, C>, dim3((unsigned)g_dq), dim3(kBwdWaves * 64),
+                      args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)attn_bwd_dkdv<E, D, C>, dim3((unsigned)g_kv),
+                         dim3(kBwdWaves * 64), args, 0, stream);
+}
+template <class E>
+hipError_t launch_backward_e(int d, bool causal, const BwdParams& p, hipStream_t s) {
+  if (d == 64) return causal ? launch_backward_t<E, 64, true>(p, s) : launch_backward_t<E, 64, false>(p, s);
+  if (d == 128) return causal ? launch_backward_t<E, 128, true>(p, s) : launch_backward_t<E, 128, false>(p, s);
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_backward(Kind kind, int d, bool causal, const BwdParams& p, hipStream_t stream) {
+  if (kind == Kind::BF16) return launch_backward_e<Bf16>(d, causal, p, stream);
+  if (kind == Kind::F16) return launch_backward_e<F16>(d, causal, p, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode(Kind kind, int d, bool causal, const DecodeParams& p, hipStream_t stream) {
   if (kind == Kind::BF16) return launch_decode_e<Bf16>(d, causal, p, stream);

@@ -42,6 +42,27 @@ struct DecodeParams {
   float c, scale_eff, o_scale;
 };
 
+// Backward: gradients of the forward with respect to Q, K and V.
+struct BwdParams {
+  const void* q;     // [B, H, N, D]
+  const void* k;     // [B, H_kv, N, D]
+  const void* v;
+  const void* o;     // forward output [B, H, N, D]
+  const void* dout;  // upstream gradient dO [B, H, N, D]
+  const float* lse;  // forward LSE [B, H, N]
+  void* dq;          // [B, H, N, D]
+  void* dk;          // [B, H_kv, N, D]
+  void* dv;
+  const int32_t* key_len;
+  float* delta;      // workspace [B*H*N]: rowsum(dO * O)
+  float* lse2;       // workspace [B*H*N]: LSE * log2(e), +inf for rows without keys
+  int B, H, H_kv, group, N;
+  int n_qt;          // 128-query tiles per head (dQ pass)
+  int n_kt;          // 128-key tiles per K/V head (dK/dV pass)
+  float c;           // scale * log2(e)
+  float scale;
+};
+
 enum class Kind { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 
 // Rows of Q owned by one workgroup for a problem's kind, d, N and mask; 0 if
@@ -56,6 +77,9 @@ hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStr
 // (K/V head, row block) pairs over Nk keys. Deterministic in its arguments:
 // the workspace size and the launch both use it.
 int decode_splits(int units_base, int Nk, int* chunk_tiles);
+
+// Enqueue the backward's three passes on `stream` (16-bit kinds only).
+hipError_t launch_backward(Kind kind, int d, bool causal, const BwdParams& p, hipStream_t stream);
 
 // Enqueue the split pass and the merge on `stream` (16-bit kinds only).
 hipError_t launch_decode(Kind kind, int d, bool causal, const DecodeParams& p, hipStream_t stream);

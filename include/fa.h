@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3  /* 2: fa_fwd_gqa; 3: fa_fwd_decode */
+#define FA_ABI_VERSION 4  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd */
 
 typedef enum {
   FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
@@ -168,6 +168,41 @@ int fa_fwd_decode(const void* Q, const void* K, const void* V, void* O, float* L
  * products out of range).
  */
 size_t fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
+
+/*
+ * fa_bwd -- gradients of fa_fwd / fa_fwd_gqa with respect to Q, K and V.
+ *
+ * The pages report training speedups (FlashAttention (ES), "Resultados
+ * empíricos") without writing the backward out; this is the calculus of the
+ * forward's definition with its masks. With P the attention probabilities:
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q,
+ * where P is recomputed from Q, K and the forward's LSE (no N x N matrix is
+ * stored). Grouped K/V heads receive the sum over the query heads sharing
+ * them.
+ *
+ *   Q, O, dO [in]  device, [B,H,N,d] of `dtype`; O and LSE as the forward
+ *                  returned them for these Q, K, V, scale, causal, key_len
+ *   K, V     [in]  device, [B,H_kv,N,d] of `dtype`
+ *   LSE      [in]  device, float [B,H,N]
+ *   dQ       [out] device, [B,H,N,d] of `dtype`
+ *   dK, dV   [out] device, [B,H_kv,N,d] of `dtype`
+ *   dtype    FA_DTYPE_BF16 or FA_DTYPE_FP16 (others: FA_ERR_UNSUPPORTED)
+ *   workspace, workspace_bytes
+ *            device scratch owned by the caller, 16-byte aligned, at least
+ *            fa_bwd_workspace_bytes(B, H, N) bytes (two floats per query row);
+ *            overlapping calls need separate workspaces.
+ *   other arguments as fa_fwd_gqa (H_kv == H for ungrouped heads).
+ * Errors as fa_fwd, plus FA_ERR_INVALID_ARG for a NULL, misaligned or too
+ * small workspace. Three kernels run in order on `stream`.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int H_kv, int N, int d,
+           float scale, int causal, const int32_t* key_len, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bwd needs (0 if a size is < 1 or the product overflows). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /* A static, human-readable name for a fa_status value (never NULL). */
 const char* fa_status_str(int status);

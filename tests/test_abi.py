@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
     assert _lib.status_name(0) == "FA_OK"
     assert _lib.status_name(-1) == "FA_ERR_INVALID_ARG"
     assert _lib.status_name(-2) == "FA_ERR_UNSUPPORTED"
