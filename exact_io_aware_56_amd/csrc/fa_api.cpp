@@ -44,7 +44,10 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   // B*H*N*d elements, and the same count in bytes for fp32, must fit in int64.
   const __int128 elems = (__int128)B * H * N * d;
   if (elems * 4 > (__int128)INT64_MAX) return fail(FA_ERR_INVALID_ARG, "B*H*N*d overflows");
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64, 128 or 256");
+  if (d == 256 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension 256 takes bfloat16 or float16 inputs");
   // Kernels address one head's K and V through 32-bit byte offsets.
   const long long head_bytes = (long long)N * d * (dtype == FA_DTYPE_FP32 ? 4 : dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2);
   if (head_bytes >= (1LL << 30)) return fail(FA_ERR_UNSUPPORTED, "one head's N x d tensor must be under 1 GiB");

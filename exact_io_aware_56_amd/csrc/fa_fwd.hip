@@ -569,6 +569,134 @@ __global__ __launch_bounds__(NW * 64, FA_WAVES_PER_EU) void attn_fwd_16bit(Param
 }
 
 // ---------------------------------------------------------------------------
+// Head dimension 256 (bf16 / fp16): each query tile is handled by two
+// workgroups, one per 128-column half of V and O. Both compute the whole S
+// (Q and K over all 256 dimensions, in the same order), so both arrive at the
+// same running maximum and sum without talking to each other; the first also
+// writes LSE. S is computed twice, so the launch executes 1.5x the nominal
+// FLOPs, but a wave keeps 128 O accumulators instead of 256 and two of these
+// workgroups fit on a CU.
+// ---------------------------------------------------------------------------
+template <class E, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_d256(Params p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  typedef T v4t __attribute__((ext_vector_type(4)));
+  constexpr int D = 256, DV = 128;      // Q/K width, V/O columns per workgroup
+  constexpr int BR = NW * 32, BC = 32;
+  constexpr int KS = D / 16, DB = DV / 32;
+  constexpr int KST = D + FA_K_SKEW, VST = DV + FA_V_SKEW;
+  constexpr int NT = NW * 64;
+  constexpr int KCPR = D / 8, VCPR = DV / 8;  // 16-byte pieces per K / V row
+  constexpr int KCH = BC * KCPR / NT, VCH = BC * VCPR / NT;
+  static_assert(BC * KCPR % NT == 0 && BC * VCPR % NT == 0, "tile pieces per thread");
+
+  __shared__ __attribute__((aligned(16))) T ks[2][BC * KST];
+  __shared__ __attribute__((aligned(16))) T vs[2][BC * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int half = blockIdx.x & 1;
+  const int logical = blockIdx.x >> 1;
+  const int bh0 = logical / p.n_qt;
+  const int qt = CAUSAL ? p.n_qt - 1 - (logical - bh0 * p.n_qt) : logical - bh0 * p.n_qt;
+  const RowRange rr = row_range_at<BR, BC, CAUSAL>(p, bh0, qt, wave, l32);
+  const int N = p.N;
+  const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;
+  const T* Kh = (const T*)p.k + kv_head;
+  const T* Vh = (const T*)p.v + kv_head + half * DV;
+
+  v8 qf[KS];
+  {
+    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, D * 2);
+    const int off = ((rr.qrow - rr.q_wg0) * D + 8 * hi) * 2;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qf[st] = __builtin_bit_cast(v8, load16(rq, off + 32 * st));
+  }
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
+  const float thr = fminf(kRescaleLog2 / p.c, 1e30f);
+
+  const int kv_lim = rr.kl;
+  i32x4 kreg[KCH], vreg[VCH];
+  auto gload = [&](int j) __attribute__((always_inline)) {
+    const auto rk = tile_rsrc(Kh, j, BC, kv_lim, D * 2);
+    // V rows keep their full 512-byte stride; the resource starts at this
+    // workgroup's column half and ends within the last row's half.
+    const int rows = max(0, min(BC, kv_lim - j * BC));
+    const auto rv = buffer_rsrc(Vh + (rows > 0 ? (size_t)j * BC * D : 0),
+                                rows > 0 ? ((rows - 1) * D + DV) * 2 : 0);
+#pragma unroll
+    for (int cc = 0; cc < KCH; ++cc) {
+      const int piece = tid + cc * NT;
+      kreg[cc] = load16(rk, ((piece / KCPR) * D + (piece % KCPR) * 8) * 2);
+    }
+#pragma unroll
+    for (int cc = 0; cc < VCH; ++cc) {
+      const int piece = tid + cc * NT;
+      vreg[cc] = load16(rv, ((piece / VCPR) * D + (piece % VCPR) * 8) * 2);
+    }
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < KCH; ++cc) {
+      const int piece = tid + cc * NT;
+      *(i32x4*)(&ks[buf][(piece / KCPR) * KST + (piece % KCPR) * 8]) = kreg[cc];
+    }
+#pragma unroll
+    for (int cc = 0; cc < VCH; ++cc) {
+      const int piece = tid + cc * NT;
+      *(i32x4*)(&vs[buf][(piece / VCPR) * VST + (piece % VCPR) * 8]) = vreg[cc];
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int j = 0; j < rr.nt; ++j) {
+    const int buf = j & 1;
+    gload(j + 1);
+    auto tile = [&](auto masked) __attribute__((always_inline)) {
+      f32x16 sc[1] = {f32x16{}};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const v8 a = *(const v8*)(ks[buf] + l32 * KST + 16 * st + 8 * hi);
+        sc[0] = E::mma(a, qf[st], sc[0]);
+      }
+      if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(sc, j * BC, rr.kl, rr.qrow, hi);
+      v8 pf[2];
+      online_softmax<E, 1, DB>(sc, p.c, thr, m, l, o, pf);
+      pv_product<E, 1, DB, VST>(vs[buf], lane, pf, o);
+    };
+    if (j < rr.wfull) tile(std::false_type{});
+    else if (j < rr.wnt) tile(std::true_type{});
+    sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = sum_halves(l);
+  const bool live = lt > 0.0f;
+  const float inv = live ? p.o_scale / lt : 0.0f;
+  if (rr.qrow < N) {
+    T* orow = (T*)p.o + ((size_t)rr.bh * N + rr.qrow) * D + half * DV;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        v4t out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (T)(o[db][4 * g + e] * inv);
+        *(v4t*)(orow + 32 * db + 8 * g + 4 * hi) = out;
+      }
+    if (half == 0 && hi == 0)
+      p.lse[(size_t)rr.bh * N + rr.qrow] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Direct-to-LDS tile copies (gfx950 buffer_load_dwordx4 ... lds, 16 bytes per
 // lane): no staging registers and no LDS write instructions. Rows are stored
 // unpadded and the 16-byte slots of each row are XOR-permuted so that the
@@ -1977,6 +2105,7 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
 }  // namespace
 
 int rows_per_block(Kind kind, int d, int N, bool causal) {
+  if (d == 256) return (kind == Kind::BF16 || kind == Kind::F16) ? 4 * 32 : 0;
   if (d != 64 && d != 128) return 0;
   if (kind == Kind::FP8 && use_pipe(N, causal)) return FA_WIDE_WAVES * 32;
   if (kind == Kind::BF16 || kind == Kind::F16) {
@@ -1989,6 +2118,18 @@ int rows_per_block(Kind kind, int d, int N, bool causal) {
 }
 
 hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream) {
+  if (d == 256) {
+    // two workgroups (column halves of O) per query tile
+    const long long grid = 2LL * p.B * p.H * p.n_qt;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    Params local = p;
+    void* args[] = {&local};
+    const void* k = nullptr;
+    if (kind == Kind::BF16) k = causal ? (const void*)attn_fwd_d256<Bf16, 4, true> : (const void*)attn_fwd_d256<Bf16, 4, false>;
+    else if (kind == Kind::F16) k = causal ? (const void*)attn_fwd_d256<F16, 4, true> : (const void*)attn_fwd_d256<F16, 4, false>;
+    else return hipErrorInvalidValue;
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(4 * 64), args, 0, stream);
+  }
   if (d == 64) return causal ? launch_d<64, true>(kind, p, stream) : launch_d<64, false>(kind, p, stream);
   if (d == 128) return causal ? launch_d<128, true>(kind, p, stream) : launch_d<128, false>(kind, p, stream);
   return hipErrorInvalidValue;

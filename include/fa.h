@@ -61,8 +61,10 @@ typedef enum {
                               out-of-range dtype, a scale or descale that is
                               not finite and > 0, sizes whose products
                               overflow, or an H_kv that does not divide H   */
-  FA_ERR_UNSUPPORTED = -2, /* a head dimension d other than 64 or 128, or
-                              one head's N x d tensor of 1 GiB or more      */
+  FA_ERR_UNSUPPORTED = -2, /* a head dimension d other than 64 or 128 (or
+                              256 with 16-bit inputs to the forward), a
+                              dtype an entry point does not take, or one
+                              head's N x d tensor of 1 GiB or more          */
   FA_ERR_HIP = -3          /* the HIP runtime refused the launch            */
 } fa_status;
 
@@ -73,8 +75,9 @@ typedef enum {
  *   O        [out] device, [B,H,N,d]; of `dtype`, or bfloat16 for fp8 input
  *   LSE      [out] device, float [B,H,N], natural-log log-sum-exp per row
  *   B, H, N  batch, heads, sequence length (queries and keys), each >= 1
- *   d        head dimension; 64 or 128 (and N*d*sizeof(element) < 2^30:
- *            one head's Q, K or V below 1 GiB)
+ *   d        head dimension; 64 or 128, or 256 for bfloat16 / float16 inputs
+ *            (and N*d*sizeof(element) < 2^30: one head's Q, K or V below
+ *            1 GiB)
  *   scale    multiplies QK^T before the mask; finite and > 0 (the pages use
  *            1/sqrt(d))
  *   causal   0 or 1 (any non-zero value means 1)
@@ -150,7 +153,8 @@ int fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *            fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d) bytes; its
  *            contents on entry do not matter and on return are undefined.
  *            Calls that overlap in time need separate workspaces.
- *   d, scale, stream as fa_fwd.
+ *   d        64 or 128
+ *   scale, stream as fa_fwd.
  *
  * The keys of each K/V head are split into chunks processed in parallel,
  * each writing a normalised partial O and its LSE to the workspace; a second
@@ -192,6 +196,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
  *            device scratch owned by the caller, 16-byte aligned, at least
  *            fa_bwd_workspace_bytes(B, H, N) bytes (two floats per query row);
  *            overlapping calls need separate workspaces.
+ *   d        64 or 128
  *   other arguments as fa_fwd_gqa (H_kv == H for ungrouped heads).
  * Errors as fa_fwd, plus FA_ERR_INVALID_ARG for a NULL, misaligned or too
  * small workspace. Three kernels run in order on `stream`.

@@ -58,8 +58,10 @@ def call(**kw):
     (dict(dtype=4), -1), (dict(dtype=-1), -1), (dict(scale=0.0), -1), (dict(scale=-1.0), -1),
     (dict(scale=math.inf), -1), (dict(scale=math.nan), -1), (dict(q=P + 8), -1),
     (dict(o=P + 4), -1), (dict(lse=P + 2), -1), (dict(key_len=P + 1), -1),
-    (dict(B=1 << 30, H=1 << 30, N=1 << 30), -1), (dict(d=96), -2), (dict(d=256), -2),
-    (dict(d=32, dtype=0), -2),
+    (dict(B=1 << 30, H=1 << 30, N=1 << 30), -1), (dict(d=96), -2), (dict(d=512), -2),
+    (dict(d=32, dtype=0), -2), (dict(d=256, dtype=0), -2), (dict(d=256, dtype=3), -2),
+    # head dimension 256 keeps one head under 1 GiB too: 2^21 rows x 256 x bf16
+    (dict(N=1 << 21, d=256), -2),
     # one head's N x d tensor must stay under 1 GiB: 2^22 rows x 128 x bf16 is exactly 1 GiB
     (dict(N=1 << 22, d=128), -2), (dict(N=(1 << 21) + 1, d=128, dtype=0), -2),
 ])
@@ -91,7 +93,8 @@ def gqa_call(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(H_kv=0), -1), (dict(H_kv=-2), -1), (dict(H_kv=3), -1), (dict(H_kv=16), -1),
     (dict(H=6, H_kv=4), -1), (dict(k=None), -1), (dict(v=P + 8), -1), (dict(qd=0.0), -1),
-    (dict(vd=math.nan), -1), (dict(dtype=5), -1), (dict(d=256), -2), (dict(d=96, H_kv=1), -2),
+    (dict(vd=math.nan), -1), (dict(dtype=5), -1), (dict(d=512), -2), (dict(d=96, H_kv=1), -2),
+    (dict(d=256, dtype=0), -2),
 ])
 def test_grouped_entry_point_rejects_bad_arguments(kw, status):
     assert gqa_call(**kw) == status

@@ -217,3 +217,23 @@ def test_grouped_kv_heads(dtype, d, N, causal, padded, H, H_kv):
     o, lse = run(w)
     o_ref, lse_ref = full_oracle(w)
     assert_close(o, lse, o_ref, lse_ref, dtype, f"H={H} H_kv={H_kv}")
+
+
+# Head dimension 256 (16-bit inputs): two workgroups per query tile, one per
+# column half of O; ragged tiles, padding, grouped heads and a longer sequence.
+D256 = [(1, False, 2, 2, 2), (33, True, 2, 3, 3), (127, False, 1, 4, 2), (300, True, 2, 2, 1),
+        (1000, False, 1, 2, 2)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256(dtype, causal):
+    for i, (N, padded, B, H, H_kv) in enumerate(D256):
+        spec = small_spec(dtype, 256, N, causal, padded, B=B, H=H,
+                          seed=9700 + 11 * i + causal).with_shape(H_kv=H_kv)
+        say(f"case d256 dtype={dtype} causal={causal} N={N} padded={padded} H={H}/{H_kv} "
+            f"seed={spec.seed}")
+        w = W.draw(spec)
+        o, lse = run(w)
+        o_ref, lse_ref = full_oracle(w)
+        assert_close(o, lse, o_ref, lse_ref, dtype, f"d256 N={N}")

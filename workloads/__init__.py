@@ -110,6 +110,9 @@ SPECS = {
     "long_causal_grouped_bf16": Spec("long_causal_grouped_bf16", 1, 32, 8192, 128, "bf16", True,
                                      1.0 / math.sqrt(128), outlier_frac=0.01, seed=20260006,
                                      H_kv=8),
+    # Head dimension 256 at the long causal decoder's FLOP count (half the heads).
+    "long_causal_d256_bf16": Spec("long_causal_d256_bf16", 1, 16, 8192, 256, "bf16", True,
+                                  1.0 / math.sqrt(256), outlier_frac=0.01, seed=20260008),
     # One new token per sequence against a 16K-key cache: 16 sequences whose
     # caches hold 8K..16K valid keys, 32 query heads over 8 K/V heads.
     "decode_grouped_bf16": Spec("decode_grouped_bf16", 16, 32, 16384, 128, "bf16", True,
