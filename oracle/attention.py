@@ -23,6 +23,12 @@ FlashAttention-2's additions. K and V may therefore carry H_kv heads with H_kv
 dividing H; query head h then takes K/V head h // (H // H_kv) (consecutive
 query heads form a group; H_kv = 1 is multi-query, H_kv = H the plain case).
 
+Sliding windows: richer masks are named in the pages only through a title in
+the bibliography of FlashAttention (ES) ("FlashMask"). The banded (local)
+mask is read as: with window = (left, right), key j is also required to
+satisfy j >= i - left and j <= i + right (a negative bound means unbounded);
+it combines with the causal and padding masks by AND.
+
 A row with no allowed key gets O_i = 0 and LSE_i = -inf. key_len is clamped to
 [0, N]; None means every key is valid. LSE is the natural-log log-sum-exp of
 the allowed scaled logits, i.e. the running maximum and running sum of
@@ -44,12 +50,18 @@ def _as64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def allowed_mask(rows: np.ndarray, N: int, causal: bool, kl: int) -> np.ndarray:
+def allowed_mask(rows: np.ndarray, N: int, causal: bool, kl: int, window=None) -> np.ndarray:
     """Boolean [len(rows), N]: which keys each query row may attend to."""
     j = np.arange(N)[None, :]
     ok = j < kl
     if causal:
         ok = ok & (j <= rows[:, None])
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            ok = ok & (j >= rows[:, None] - left)
+        if right >= 0:
+            ok = ok & (j <= rows[:, None] + right)
     return ok
 
 
@@ -60,10 +72,10 @@ def clamp_key_len(key_len, b: int, N: int) -> int:
 
 
 def masked_scores(q_rows: np.ndarray, k: np.ndarray, scale: float, rows: np.ndarray,
-                  causal: bool, kl: int) -> np.ndarray:
+                  causal: bool, kl: int, window=None) -> np.ndarray:
     """scale * q_rows @ k.T with -inf where the mask forbids the pair (float64)."""
     s = float(scale) * (_as64(q_rows) @ _as64(k).T)
-    ok = allowed_mask(rows, k.shape[0], causal, kl)
+    ok = allowed_mask(rows, k.shape[0], causal, kl, window)
     return np.where(ok, s, -np.inf)
 
 
@@ -79,8 +91,8 @@ def softmax_stats(s: np.ndarray):
     return p, m, l
 
 
-def _rows_forward(q_rows, k, v, scale, rows, causal, kl):
-    s = masked_scores(q_rows, k, scale, rows, causal, kl)
+def _rows_forward(q_rows, k, v, scale, rows, causal, kl, window=None):
+    s = masked_scores(q_rows, k, scale, rows, causal, kl, window)
     p, m, l = softmax_stats(s)
     o = p @ _as64(v)
     with np.errstate(divide="ignore"):
@@ -96,7 +108,8 @@ def kv_head(h: int, H: int, H_kv: int) -> int:
 
 
 def attention_forward(q, k, v, scale: float, causal: bool = False,
-                      key_len: Optional[Sequence[int]] = None, row_block: int = 2048):
+                      key_len: Optional[Sequence[int]] = None, row_block: int = 2048,
+                      window=None):
     """O [B,H,N,d] and LSE [B,H,N] (float64) for q [B,H,N,d] and k, v [B,H_kv,N,d]."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, d = q.shape
@@ -110,19 +123,19 @@ def attention_forward(q, k, v, scale: float, causal: bool = False,
                 rows = np.arange(r0, min(N, r0 + row_block))
                 g = kv_head(h, H, H_kv)
                 o[b, h, rows], lse[b, h, rows] = _rows_forward(
-                    q[b, h, rows], k[b, g], v[b, g], scale, rows, causal, kl)
+                    q[b, h, rows], k[b, g], v[b, g], scale, rows, causal, kl, window)
     return o, lse
 
 
 def attention_rows(q, k, v, scale: float, causal: bool, key_len, b: int, h: int,
-                   rows: Sequence[int]):
+                   rows: Sequence[int], window=None):
     """O and LSE of selected query rows of one (b, h), each row against its full row."""
     rows = np.asarray(rows, dtype=np.int64)
     N = q.shape[2]
     kl = clamp_key_len(key_len, b, N)
     g = kv_head(h, q.shape[1], k.shape[1])
     return _rows_forward(_as64(q[b, h, rows]), _as64(k[b, g]), _as64(v[b, g]), scale, rows,
-                         causal, kl)
+                         causal, kl, window)
 
 
 def attention_decode(q, k, v, scale: float, causal: bool = False,

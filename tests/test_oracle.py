@@ -279,11 +279,11 @@ def _brute_check(monkeypatch_fn=None):
 
 
 MUTANTS = {
-    "strict_causal": lambda rows, N, causal, kl: (
+    "strict_causal": lambda rows, N, causal, kl, window=None: (
         (np.arange(N)[None, :] < kl) & (np.arange(N)[None, :] < rows[:, None])),
-    "key_len_off_by_one": lambda rows, N, causal, kl: (
+    "key_len_off_by_one": lambda rows, N, causal, kl, window=None: (
         (np.arange(N)[None, :] <= kl) & (np.arange(N)[None, :] <= rows[:, None])),
-    "mask_ignored": lambda rows, N, causal, kl: np.ones((len(rows), N), bool),
+    "mask_ignored": lambda rows, N, causal, kl, window=None: np.ones((len(rows), N), bool),
 }
 
 
@@ -297,10 +297,10 @@ def test_pins_catch_planted_mask_mistakes(monkeypatch, name):
 def test_pins_catch_planted_arithmetic_mistakes(monkeypatch):
     orig = oatt.masked_scores
 
-    def no_scale(q_rows, k, scale, rows, causal, kl):
-        return orig(q_rows, k, 1.0, rows, causal, kl)
+    def no_scale(q_rows, k, scale, rows, causal, kl, window=None):
+        return orig(q_rows, k, 1.0, rows, causal, kl, window)
 
-    def transposed(q_rows, k, scale, rows, causal, kl):
+    def transposed(q_rows, k, scale, rows, causal, kl, window=None):
         s = float(scale) * (np.asarray(k, np.float64) @ np.asarray(q_rows, np.float64).T)
         return np.where(oatt.allowed_mask(rows, k.shape[0], causal, kl), s, -np.inf)
 
@@ -485,3 +485,68 @@ def test_single_query_decode_sees_every_valid_key():
     a = oracle.attention_decode(q, k, v, 0.5, True, key_len)
     b = oracle.attention_decode(q, k, v, 0.5, False, key_len)
     assert np.abs(a[0] - b[0]).max() == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Sliding-window (banded) masks
+
+def brute_force_window(q, k, v, scale, causal, key_len, left, right):
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    L = np.zeros((B, H, N))
+    for b in range(B):
+        kl = N if key_len is None else min(max(int(key_len[b]), 0), N)
+        for h in range(H):
+            for i in range(N):
+                allowed = [j for j in range(N) if j < kl and (not causal or j <= i)
+                           and (left < 0 or j >= i - left) and (right < 0 or j <= i + right)]
+                if not allowed:
+                    L[b, h, i] = -np.inf
+                    continue
+                w = {j: mpmath.exp(mpmath.mpf(scale) * mpmath.fsum(
+                    mpmath.mpf(float(q[b, h, i, t])) * mpmath.mpf(float(k[b, h, j, t]))
+                    for t in range(d))) for j in allowed}
+                z = mpmath.fsum(w.values())
+                for t in range(d):
+                    O[b, h, i, t] = float(mpmath.fsum(w[j] * mpmath.mpf(float(v[b, h, j, t]))
+                                                      for j in allowed) / z)
+                L[b, h, i] = float(mpmath.log(z))
+    return O, L
+
+
+@pytest.mark.parametrize("causal,left,right", [(True, 3, -1), (False, 2, 4), (False, -1, 1),
+                                               (True, 0, -1)])
+def test_window_matches_brute_force(causal, left, right):
+    rng = np.random.default_rng(70 + left + 3 * right + causal)
+    q, k, v = rand_qkv(rng, 2, 2, 13, 4)
+    key_len = np.array([13, 9])
+    O, L = oracle.attention_forward(q, k, v, 0.5, causal, key_len, window=(left, right))
+    O2, L2 = brute_force_window(q, k, v, 0.5, causal, key_len, left, right)
+    assert np.abs(O - O2).max() <= 1e-13
+    lse_close(L, L2, 1e-13)
+
+
+def test_wide_window_is_no_window_and_zero_window_is_self():
+    rng = np.random.default_rng(71)
+    q, k, v = rand_qkv(rng, 1, 2, 20, 8)
+    a = oracle.attention_forward(q, k, v, 0.3, True, window=(19, -1))
+    b = oracle.attention_forward(q, k, v, 0.3, True)
+    assert np.abs(a[0] - b[0]).max() == 0.0
+    O, L = oracle.attention_forward(q, k, v, 0.3, True, window=(0, -1))
+    assert np.abs(O - v).max() <= 1e-15
+    assert np.abs(L - 0.3 * np.einsum("bhnd,bhnd->bhn", q, k)).max() <= 1e-12
+
+
+def test_window_matches_torch_sdpa_band_mask():
+    rng = np.random.default_rng(72)
+    B, H, N, d = 2, 3, 40, 16
+    q, k, v = rand_qkv(rng, B, H, N, d)
+    key_len = np.array([40, 31])
+    O, _ = oracle.attention_forward(q, k, v, 0.25, False, key_len, window=(5, 7))
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    band = (j >= i - 5) & (j <= i + 7)
+    mask = band[None, None] & (j[None, None] < torch.as_tensor(key_len)[:, None, None, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=0.25)
+    assert np.abs(O - ref.numpy()).max() <= 1e-12
