@@ -153,7 +153,8 @@ def cpu_baseline(w, budget_s: float):
             kb = None if kl is None else kl[b:b + 1]
             g = h // (s.H // s.kv_heads)
             oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1],
-                                     v[b:b + 1, g:g + 1], s.scale, s.causal, kb)
+                                     v[b:b + 1, g:g + 1], s.scale, s.causal, kb,
+                                     window=(s.window_left, -1) if s.window_left >= 0 else None)
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -240,6 +241,9 @@ def main(argv=None):
         if args.backward:
             fa.fa_bwd(q, k, v, o_f, dout, lse_f, *grads, ws, spec.scale, spec.causal, kl,
                       stream=stream)
+        elif spec.window_left >= 0:
+            fa.fa_fwd_window(q, k, v, o, lse, spec.scale, spec.causal, (spec.window_left, -1), kl,
+                             *w.descale, stream=stream)
         elif spec.is_decode:
             fa.fa_fwd_decode(q, k, v, o, lse, ws, spec.scale, spec.causal, kl, stream=stream)
         elif spec.kv_heads != spec.H:
@@ -320,7 +324,7 @@ def main(argv=None):
         "config": {
             "workload": spec.name, "B": spec.B, "H": spec.H, "N": spec.N, "d": spec.d,
             "causal": spec.causal, "scale": spec.scale,
-            "H_kv": spec.kv_heads, "Nq": spec.q_len,
+            "H_kv": spec.kv_heads, "Nq": spec.q_len, "window_left": spec.window_left,
             "key_len": None if w.key_len is None else "per-batch padding",
             "outlier_keys_frac": spec.outlier_frac, "seed": spec.seed,
             "launch_ms_p10": round(per[len(per) // 10], 5),

@@ -1,7 +1,7 @@
 """Exact IO-aware attention forward for AMD Instinct MI355X (gfx950).
 
 Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_gqa`` /
-``fa_fwd_decode`` / ``fa_bwd`` marshal torch tensors' device pointers and the current stream
+``fa_fwd_window`` / ``fa_fwd_decode`` / ``fa_bwd`` marshal torch tensors' device pointers and the current stream
 into the C entry points of the same names; ``fwd`` (and its positional twin ``forward``) additionally
 allocates O and LSE. Nothing here computes any part of the attention.
 """
@@ -98,15 +98,29 @@ def fa_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool = False,
                                     _stream(stream)))
 
 
+def fa_fwd_window(q, k, v, o, lse, scale: float, causal: bool = False, window=(-1, -1),
+                  key_len: Optional[torch.Tensor] = None, q_descale: float = 1.0,
+                  k_descale: float = 1.0, v_descale: float = 1.0, stream=None) -> None:
+    """Enqueue fa_fwd_window: the grouped forward with a (left, right) band."""
+    _check_inputs(q, k, v, o, lse, key_len, grouped=True)
+    B, H, N, d = q.shape
+    _lib._check(_lib.fa_fwd_window_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                                       k.shape[1], N, d, scale, causal, window[0], window[1],
+                                       _ptr(key_len), _DTYPE[q.dtype], q_descale, k_descale,
+                                       v_descale, _stream(stream)))
+
+
 def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
             descale: Tuple[float, float, float] = (1.0, 1.0, 1.0),
-            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+            stream=None, window=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Allocate O and LSE on q's device and run the forward; returns (O, LSE).
     k and v with fewer heads than q take the grouped entry point."""
     B, H, N, d = q.shape
     o = torch.empty((B, H, N, d), dtype=out_dtype(q.dtype), device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if k.dim() == 4 and k.shape[1] != H:
+    if window is not None:
+        fa_fwd_window(q, k, v, o, lse, scale, causal, window, key_len, *descale, stream=stream)
+    elif k.dim() == 4 and k.shape[1] != H:
         fa_fwd_gqa(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
     elif q.dtype == torch.float8_e4m3fn:
         fa_fwd_fp8(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
@@ -117,7 +131,7 @@ def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
 
 def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
         descale: Tuple[float, float, float] = (1.0, 1.0, 1.0),
-        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        stream=None, window=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """softmax(scale * Q K^T + mask) V and its row log-sum-exp, as (O, LSE).
 
     Keyword-only form of ``forward``. q, k, v: contiguous device tensors
@@ -126,7 +140,7 @@ def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
     key_len: optional device int32 [B] of valid key counts. O has q's dtype
     (bfloat16 for fp8 inputs); LSE is float32 [B, H, N], natural log.
     """
-    return forward(q, k, v, scale, causal, key_len, descale, stream)
+    return forward(q, k, v, scale, causal, key_len, descale, stream, window)
 
 
 def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool = False,

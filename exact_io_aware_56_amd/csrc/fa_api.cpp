@@ -27,7 +27,7 @@ bool positive_finite(float x) { return isfinite(x) && x > 0.0f; }
 
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
             int H_kv, int N, int d, float scale, int causal, const int32_t* key_len, int dtype,
-            float qd, float kd, float vd, void* stream) {
+            float qd, float kd, float vd, void* stream, int win_left = -1, int win_right = -1) {
   g_last_error[0] = '\0';
   if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N and d must be >= 1");
@@ -48,12 +48,15 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
     return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64, 128 or 256");
   if (d == 256 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16)
     return fail(FA_ERR_UNSUPPORTED, "head dimension 256 takes bfloat16 or float16 inputs");
+  const bool window = win_left >= 0 || win_right >= 0;
+  if (window && ((dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) || d == 256))
+    return fail(FA_ERR_UNSUPPORTED, "sliding windows take bfloat16 or float16 inputs with d 64 or 128");
   // Kernels address one head's K and V through 32-bit byte offsets.
   const long long head_bytes = (long long)N * d * (dtype == FA_DTYPE_FP32 ? 4 : dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2);
   if (head_bytes >= (1LL << 30)) return fail(FA_ERR_UNSUPPORTED, "one head's N x d tensor must be under 1 GiB");
 
   const fa::Kind kind = static_cast<fa::Kind>(dtype);
-  const int rows = fa::rows_per_block(kind, d, N, causal != 0);
+  const int rows = fa::rows_per_block(kind, d, N, causal != 0, window);
   fa::Params p;
   p.q = Q;
   p.k = K;
@@ -72,6 +75,8 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   if (!positive_finite(p.scale_eff)) return fail(FA_ERR_INVALID_ARG, "scale*q_descale*k_descale is not finite and > 0");
   p.c = (float)((double)p.scale_eff * 1.4426950408889634);
   p.o_scale = vd;
+  p.win_left = win_left < 0 ? -1 : win_left;
+  p.win_right = win_right < 0 ? -1 : win_right;
 
   const hipError_t e = fa::launch_forward(kind, d, causal != 0, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -282,6 +287,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            size_t workspace_bytes, void* stream) {
   return backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H_kv, N, d, scale, causal, key_len, dtype,
                   workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                  int H_kv, int N, int d, float scale, int causal, int window_left,
+                  int window_right, const int32_t* key_len, int dtype, float q_descale,
+                  float k_descale, float v_descale, void* stream) {
+  return forward(Q, K, V, O, LSE, B, H, H_kv, N, d, scale, causal, key_len, dtype, q_descale,
+                 k_descale, v_descale, stream, window_left, window_right);
 }
 
 const char* fa_status_str(int status) {

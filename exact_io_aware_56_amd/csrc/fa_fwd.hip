@@ -29,6 +29,7 @@
 // Scores stay raw (unscaled) in registers; scale*log2(e) is folded into one
 // FMA ahead of v_exp_f32 (exp2), so exp(scale*s - m) = exp2(c*s - c*m).
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -360,6 +361,24 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[SB], int k0, int kl, int 
     for (int i = 0; i < 16; ++i) {
       const int c = 32 * sb + 8 * (i >> 2) + (i & 3);
       s[sb][i] = c < lim ? s[sb][i] : -INFINITY;
+    }
+}
+
+// The banded mask on top of apply_mask's: keys below qrow - win_left or above
+// qrow + win_right (a negative bound is no bound) become -inf as well.
+template <int SB, bool CAUSAL>
+__device__ __forceinline__ void apply_mask_window(f32x16 (&s)[SB], int k0, int kl, int qrow, int hi,
+                                                  int win_left, int win_right) {
+  int lim = kl - k0 - 4 * hi;
+  if (CAUSAL) lim = min(lim, qrow - k0 - 4 * hi + 1);
+  if (win_right >= 0) lim = min(lim, qrow + win_right - k0 - 4 * hi + 1);
+  const int lo = win_left >= 0 ? qrow - win_left - k0 - 4 * hi : INT_MIN / 2;
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 32 * sb + 8 * (i >> 2) + (i & 3);
+      s[sb][i] = (c < lim && c >= lo) ? s[sb][i] : -INFINITY;
     }
 }
 
@@ -764,7 +783,7 @@ __device__ __forceinline__ void wait_vmem_keep() {
 // operand reads and their latency in front of each MFMA, not the arithmetic,
 // bound the register-staged kernel above; this one trims them.
 // ---------------------------------------------------------------------------
-template <class E, int D, int BC, int NW, int NBUF, bool CAUSAL>
+template <class E, int D, int BC, int NW, int NBUF, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   using T = typename E::T;
   using v8 = typename E::v8;
@@ -797,8 +816,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
+  RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
   const int N = p.N;
+  // Sliding window: the workgroup streams tiles [t0, nt); this wave computes
+  // [wt0, wnt) of them, of which [whead, wfull) need no mask.
+  int t0 = 0, wt0 = 0, whead = 0;
+  if constexpr (WIN) {
+    const int wl = p.win_left, wr = p.win_right;
+    const int qw0 = rr.q_wg0 + 32 * wave;
+    if (wl >= 0) {
+      t0 = max(0, rr.q_wg0 - wl) / BC;
+      wt0 = max(0, qw0 - wl) / BC;
+      whead = (max(0, qw0 + 31 - wl) + BC - 1) / BC;
+    }
+    if (wr >= 0) {
+      rr.nt = min(rr.nt, (min(rr.kl, rr.q_wg0 + BR + wr) + BC - 1) / BC);
+      rr.wnt = min(rr.wnt, (max(0, min(rr.kl, qw0 + 32 + wr)) + BC - 1) / BC);
+      rr.wfull = min(rr.wfull, max(0, qw0 + wr + 1) / BC);
+    }
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+  }
   const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;
   const T* Kh = (const T*)p.k + kv_head;
   const T* Vh = (const T*)p.v + kv_head;
@@ -869,7 +906,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
     v8 vring[LA + 1];
 #pragma unroll
     for (int t = 0; t < LA; ++t) vring[t] = vfrag(vb, t);
-    if constexpr (decltype(masked)::value) apply_mask<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi);
+    if constexpr (decltype(masked)::value) {
+      if constexpr (WIN)
+        apply_mask_window<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi, p.win_left, p.win_right);
+      else
+        apply_mask<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi);
+    }
     v8 pf[PS];
     online_softmax<E, SB, DB>(s, p.c, thr, m, l, o, pf);
     // O += P V, operand reads LA steps ahead
@@ -890,27 +932,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
                   unsigned char* vn) __attribute__((always_inline)) {
     copy_tile(Kh, j + NBUF - 1, kn, std::false_type{});
     copy_tile(Vh, j + NBUF - 1, vn, std::true_type{});
-    if (j < rr.wfull) tile(j, kc, vc, std::false_type{});
-    else if (j < rr.wnt) tile(j, kc, vc, std::true_type{});
+    if constexpr (WIN) {
+      if (j >= wt0 && j < rr.wnt) {
+        if (j >= whead && j < rr.wfull) tile(j, kc, vc, std::false_type{});
+        else tile(j, kc, vc, std::true_type{});
+      }
+    } else {
+      if (j < rr.wfull) tile(j, kc, vc, std::false_type{});
+      else if (j < rr.wnt) tile(j, kc, vc, std::true_type{});
+    }
     wait_vmem_keep<KEEP>();
     __syncthreads();
   };
 
-  copy_tile(Kh, 0, k0s, std::false_type{});
-  copy_tile(Vh, 0, v0s, std::true_type{});
+  // Tiles are numbered from t0 (0 without a window); buffers follow j - t0.
+  copy_tile(Kh, t0, k0s, std::false_type{});
+  copy_tile(Vh, t0, v0s, std::true_type{});
   if constexpr (NBUF == 3) {
-    copy_tile(Kh, 1, k1s, std::false_type{});
-    copy_tile(Vh, 1, v1s, std::true_type{});
+    copy_tile(Kh, t0 + 1, k1s, std::false_type{});
+    copy_tile(Vh, t0 + 1, v1s, std::true_type{});
   }
   wait_vmem_keep<KEEP>();
   __syncthreads();
   if constexpr (NBUF == 2) {
-    for (int j = 0; j < rr.nt; j += 2) {
+    for (int j = t0; j < rr.nt; j += 2) {
       step(j, k0s, v0s, k1s, v1s);
       if (j + 1 < rr.nt) step(j + 1, k1s, v1s, k0s, v0s);
     }
   } else {
-    for (int j = 0; j < rr.nt; j += 3) {
+    for (int j = t0; j < rr.nt; j += 3) {
       step(j, k0s, v0s, k2s, v2s);
       if (j + 1 < rr.nt) step(j + 1, k1s, v1s, k0s, v0s);
       if (j + 2 < rr.nt) step(j + 2, k2s, v2s, k1s, v1s);
@@ -2075,6 +2125,9 @@ bool use_pipe(int N, bool causal) {
 
 template <class E, int D, bool C>
 hipError_t launch_16bit(const Params& p, hipStream_t s) {
+  if (p.win_left >= 0 || p.win_right >= 0)
+    return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C, true>, p,
+                  FA_DMA_WAVES * 64, s);
   if (use_pipe(p.N, C))
     return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false>, p,
                   FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
@@ -2104,9 +2157,10 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
 
 }  // namespace
 
-int rows_per_block(Kind kind, int d, int N, bool causal) {
-  if (d == 256) return (kind == Kind::BF16 || kind == Kind::F16) ? 4 * 32 : 0;
+int rows_per_block(Kind kind, int d, int N, bool causal, bool window) {
+  if (d == 256) return (kind == Kind::BF16 || kind == Kind::F16) && !window ? 4 * 32 : 0;
   if (d != 64 && d != 128) return 0;
+  if (window) return (kind == Kind::BF16 || kind == Kind::F16) ? FA_DMA_WAVES * 32 : 0;
   if (kind == Kind::FP8 && use_pipe(N, causal)) return FA_WIDE_WAVES * 32;
   if (kind == Kind::BF16 || kind == Kind::F16) {
     if (use_pipe(N, causal)) return FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS;

@@ -21,6 +21,8 @@ struct Params {
   float c;          // scale_eff * log2(e): multiplies raw scores before exp2
   float scale_eff;  // scale * q_descale * k_descale
   float o_scale;    // v_descale
+  int win_left;     // sliding window: keys j >= i - win_left (negative: unbounded)
+  int win_right;    // and j <= i + win_right (negative: unbounded)
 };
 
 // Decode (few queries against a key/value cache), split over keys.
@@ -67,7 +69,7 @@ enum class Kind { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 
 // Rows of Q owned by one workgroup for a problem's kind, d, N and mask; 0 if
 // d is unsupported. Must agree with the kernel launch_forward picks.
-int rows_per_block(Kind kind, int d, int N, bool causal);
+int rows_per_block(Kind kind, int d, int N, bool causal, bool window = false);
 
 // Enqueue the forward on `stream`. Arguments are already validated and
 // p.n_qt filled in. Returns the launch's hipError_t.

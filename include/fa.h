@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd */
+#define FA_ABI_VERSION 5  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd; 5: fa_fwd_window */
 
 typedef enum {
   FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
@@ -129,6 +129,22 @@ int fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int H, int H_kv, int N, int d, float scale, int causal,
                const int32_t* key_len, int dtype, float q_descale, float k_descale,
                float v_descale, void* stream);
+
+/*
+ * fa_fwd_window -- fa_fwd_gqa with a sliding-window (banded) mask on top of
+ * the causal and padding masks (richer masks appear in the pages only as the
+ * FlashMask title in the bibliography of FlashAttention (ES)): key j is
+ * allowed for query i only if also
+ *     window_left < 0  or j >= i - window_left
+ *     window_right < 0 or j <= i + window_right
+ * (a negative bound is no bound). Key tiles wholly outside every row's band
+ * are skipped. bfloat16 / float16 inputs with d 64 or 128 (others:
+ * FA_ERR_UNSUPPORTED); other arguments as fa_fwd_gqa.
+ */
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  int B, int H, int H_kv, int N, int d, float scale, int causal,
+                  int window_left, int window_right, const int32_t* key_len, int dtype,
+                  float q_descale, float k_descale, float v_descale, void* stream);
 
 /*
  * fa_fwd_decode -- the newest Nq queries of each batch entry against its

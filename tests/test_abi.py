@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
     assert _lib.status_name(0) == "FA_OK"
     assert _lib.status_name(-1) == "FA_ERR_INVALID_ARG"
     assert _lib.status_name(-2) == "FA_ERR_UNSUPPORTED"
@@ -132,6 +132,25 @@ def test_decode_workspace_size():
     # covers one partial O row and LSE per (query row, chunk)
     rows = 2 * 8 * 1
     assert n >= rows * 4 * (128 + 1)
+
+
+def window_call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, H_kv=2, N=64, d=64, scale=0.125, causal=1,
+             wl=16, wr=-1, key_len=None, dtype=2, qd=1.0, kd=1.0, vd=1.0, stream=None)
+    a.update(kw)
+    return _lib.fa_fwd_window_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                  a["H_kv"], a["N"], a["d"], a["scale"], a["causal"], a["wl"],
+                                  a["wr"], a["key_len"], a["dtype"], a["qd"], a["kd"], a["vd"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), -2), (dict(dtype=3), -2), (dict(d=256), -2), (dict(H_kv=3), -1),
+    (dict(q=None), -1), (dict(scale=0.0), -1), (dict(wr=5, d=96), -2),
+])
+def test_window_entry_point_rejects_bad_arguments(kw, status):
+    assert window_call(**kw) == status
+    assert _lib.load().fa_last_error().decode() != ""
 
 
 def test_python_binding_names_the_entry_points():

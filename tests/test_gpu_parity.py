@@ -12,9 +12,10 @@ import numpy as np
 import pytest
 import torch
 
+import exact_io_aware_56_amd as fa
 import oracle
 import workloads as W
-from parity import assert_close, full_oracle, run, sampled_rows, say
+from parity import assert_close, full_oracle, run, sampled_rows, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -237,3 +238,31 @@ def test_head_dim_256(dtype, causal):
         o, lse = run(w)
         o_ref, lse_ref = full_oracle(w)
         assert_close(o, lse, o_ref, lse_ref, dtype, f"d256 N={N}")
+
+
+# Sliding windows (fa_fwd_window): bands on either side, with and without the
+# causal mask, ragged lengths, padding and grouped heads.
+WINDOWS = [  # causal, (left, right)
+    (True, (0, -1)), (True, (63, -1)), (True, (100, -1)), (False, (5, 7)), (False, (-1, 3)),
+    (False, (130, 0)), (True, (1000, -1))]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_sliding_window(dtype, d):
+    for i, (causal, window) in enumerate(WINDOWS):
+        for N, padded in ((1, False), (65, True), (300, False), (1000, True)):
+            H_kv = 1 if i % 2 else 2
+            spec = small_spec(dtype, d, N, causal, padded, B=2, H=2,
+                              seed=9900 + 7 * i + N + d).with_shape(H_kv=H_kv)
+            say(f"case window dtype={dtype} d={d} causal={causal} window={window} N={N} "
+                f"padded={padded} H_kv={H_kv} seed={spec.seed}")
+            w = W.draw(spec)
+            q, k, v, kl = to_device(w)
+            o, lse = fa.fwd(q, k, v, scale=spec.scale, causal=causal, key_len=kl, window=window)
+            torch.cuda.synchronize()
+            qe, ke, ve = w.exact()
+            o_ref, lse_ref = oracle.attention_forward(qe, ke, ve, spec.scale, causal,
+                                                      w.key_len_or_none(), window=window)
+            assert_close(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref,
+                         dtype, f"window={window} N={N}")

@@ -61,6 +61,7 @@ class Spec:
     seed: int = 0
     H_kv: Optional[int] = None  # K/V heads (None: H, no grouping)
     Nq: Optional[int] = None    # decode: queries per head against N cached keys
+    window_left: int = -1       # causal sliding window: keys j >= i - window_left
 
     @property
     def is_decode(self) -> bool:
@@ -79,6 +80,8 @@ class Spec:
         4*B*H*Nq*N*d (every query against the whole cache)."""
         if self.is_decode:
             return 4.0 * self.B * self.H * self.Nq * self.N * self.d
+        if self.window_left >= 0 and self.causal:
+            return 4.0 * self.B * self.H * self.d * self._band_pairs()
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
@@ -86,8 +89,17 @@ class Spec:
         """Nominal exponentials (one per score): B*H*N^2, halved when causal."""
         if self.is_decode:
             return float(self.B) * self.H * self.Nq * self.N
+        if self.window_left >= 0 and self.causal:
+            return float(self.B) * self.H * self._band_pairs()
         e = float(self.B) * self.H * self.N * self.N
         return e / 2 if self.causal else e
+
+    def _band_pairs(self) -> float:
+        """(query, key) pairs of a causal band of width window_left + 1."""
+        w, n = self.window_left + 1, self.N
+        if w >= n:
+            return n * (n + 1) / 2.0
+        return w * (w + 1) / 2.0 + (n - w) * float(w)
 
     def with_shape(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -113,6 +125,10 @@ SPECS = {
     # Head dimension 256 at the long causal decoder's FLOP count (half the heads).
     "long_causal_d256_bf16": Spec("long_causal_d256_bf16", 1, 16, 8192, 256, "bf16", True,
                                   1.0 / math.sqrt(256), outlier_frac=0.01, seed=20260008),
+    # The long causal decoder shape with a 1024-key sliding window.
+    "long_causal_window_bf16": Spec("long_causal_window_bf16", 1, 32, 8192, 128, "bf16", True,
+                                    1.0 / math.sqrt(128), outlier_frac=0.01, seed=20260009,
+                                    window_left=1023),
     # One new token per sequence against a 16K-key cache: 16 sequences whose
     # caches hold 8K..16K valid keys, 32 query heads over 8 K/V heads.
     "decode_grouped_bf16": Spec("decode_grouped_bf16", 16, 32, 16384, 128, "bf16", True,
