@@ -207,7 +207,8 @@ int backward(const void* Q, const void* K, const void* V, const void* O, const v
   const long long need = bwd_workspace(B, H, N);
   if (need == 0 || (long long)workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_bwd_workspace_bytes()");
-  const long long tiles = (N + 127) / 128;
+  const int bwd_rows = fa::bwd_rows_per_block();
+  const long long tiles = (N + bwd_rows - 1) / bwd_rows;
   if ((long long)B * H * tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "grid too large");
 
   fa::BwdParams p;

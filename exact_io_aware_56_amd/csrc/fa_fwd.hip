@@ -1800,7 +1800,10 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 // an accumulator (dQ from dS^T, dV from P, dK from dS) use pv_product, the
 // forward's transposing-read product.
 // ---------------------------------------------------------------------------
-constexpr int kBwdWaves = 4;               // waves per workgroup
+#ifndef FA_BWD_WAVES
+#define FA_BWD_WAVES 4  // waves per workgroup of the backward passes
+#endif
+constexpr int kBwdWaves = FA_BWD_WAVES;    // waves per workgroup
 constexpr int kBwdRows = kBwdWaves * 32;   // query rows (dQ) or keys (dK/dV) per workgroup
 constexpr int kBwdSkew = 32;               // extra 16-bit elements per LDS row
 
@@ -1851,7 +1854,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, ST = D + kBwdSkew;
   constexpr int NT = kBwdWaves * 64;
   constexpr int CH = (32 * CPR + NT - 1) / NT;  // 16-byte pieces per thread per tile
-  static_assert(32 * CPR % NT == 0, "tile pieces split evenly over the threads");
+  constexpr bool kRagged = 32 * CPR % NT != 0;  // some threads idle on the last piece
   __shared__ __attribute__((aligned(16))) T ks[2][32 * ST];
   __shared__ __attribute__((aligned(16))) T vs[2][32 * ST];
 
@@ -1904,6 +1907,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq(BwdParams p) {
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       const int piece = tid + cc * NT;
+      if (kRagged && piece >= 32 * CPR) continue;
       const int off = ((piece / CPR) * D + (piece % CPR) * 8) * 2;
       kreg[cc] = load16(rk, off);
       vreg[cc] = load16(rv, off);
@@ -1913,6 +1917,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq(BwdParams p) {
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       const int piece = tid + cc * NT;
+      if (kRagged && piece >= 32 * CPR) continue;
       const int r = piece / CPR, col = (piece % CPR) * 8;
       *(i32x4*)(&ks[buf][r * ST + col]) = kreg[cc];
       *(i32x4*)(&vs[buf][r * ST + col]) = vreg[cc];
@@ -1965,7 +1970,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dkdv(BwdParams p) 
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, ST = D + kBwdSkew;
   constexpr int NT = kBwdWaves * 64;
   constexpr int CH = (32 * CPR + NT - 1) / NT;
-  static_assert(32 * CPR % NT == 0, "tile pieces split evenly over the threads");
+  constexpr bool kRagged = 32 * CPR % NT != 0;
   __shared__ __attribute__((aligned(16))) T qs[2][32 * ST];
   __shared__ __attribute__((aligned(16))) T dos[2][32 * ST];
   __shared__ __attribute__((aligned(16))) float ls[2][32];
@@ -2018,6 +2023,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dkdv(BwdParams p) 
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       const int piece = tid + cc * NT;
+      if (kRagged && piece >= 32 * CPR) continue;
       const int off = ((piece / CPR) * D + (piece % CPR) * 8) * 2;
       qreg[cc] = load16(rq, off);
       dreg[cc] = load16(rd, off);
@@ -2033,6 +2039,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dkdv(BwdParams p) 
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       const int piece = tid + cc * NT;
+      if (kRagged && piece >= 32 * CPR) continue;
       const int r = piece / CPR, col = (piece % CPR) * 8;
       *(i32x4*)(&qs[buf][r * ST + col]) = qreg[cc];
       *(i32x4*)(&dos[buf][r * ST + col]) = dreg[cc];
@@ -2249,6 +2256,8 @@ hipError_t launch_backward_e(int d, bool causal, const BwdParams& p, hipStream_t
   return hipErrorInvalidValue;
 }
 }  // namespace
+
+int bwd_rows_per_block() { return kBwdRows; }
 
 hipError_t launch_backward(Kind kind, int d, bool causal, const BwdParams& p, hipStream_t stream) {
   if (kind == Kind::BF16) return launch_backward_e<Bf16>(d, causal, p, stream);

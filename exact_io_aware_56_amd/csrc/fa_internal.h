@@ -80,6 +80,9 @@ hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStr
 // the workspace size and the launch both use it.
 int decode_splits(int units_base, int Nk, int* chunk_tiles);
 
+// Query rows (dQ pass) and keys (dK/dV pass) per backward workgroup.
+int bwd_rows_per_block();
+
 // Enqueue the backward's three passes on `stream` (16-bit kinds only).
 hipError_t launch_backward(Kind kind, int d, bool causal, const BwdParams& p, hipStream_t stream);
 
