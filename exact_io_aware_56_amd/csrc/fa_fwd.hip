@@ -1800,6 +1800,15 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 // an accumulator (dQ from dS^T, dV from P, dK from dS) use pv_product, the
 // forward's transposing-read product.
 // ---------------------------------------------------------------------------
+#ifndef FA_BWD_DMA
+#define FA_BWD_DMA 1  // backward passes on direct-to-LDS copies (0: register-staged tiles)
+#endif
+#ifndef FA_BWD_KV_OCC
+#define FA_BWD_KV_OCC 2  // waves per SIMD the dK/dV pass is compiled for (1: 512 registers)
+#endif
+#ifndef FA_BWD_LOOKAHEAD
+#define FA_BWD_LOOKAHEAD 2  // backward passes: LDS operand reads issued this many MFMAs ahead
+#endif
 #ifndef FA_BWD_WAVES
 #define FA_BWD_WAVES 4  // waves per workgroup of the backward passes
 #endif
@@ -2101,6 +2110,320 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dkdv(BwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
+// Backward passes on direct-to-LDS copies: the same arithmetic as attn_bwd_dq /
+// attn_bwd_dkdv, but the streamed 32-row tiles reach LDS through
+// buffer_load ... lds (no staging registers), three buffers deep, so a tile's
+// copy is issued two iterations before it is used. Every tile is stored with
+// the V-operand slot permutation (v_swz): transposing reads use it as the
+// forward's V reads do, and row reads (the A operands of S and dP) look their
+// 16-byte slot up through the same permutation.
+// ---------------------------------------------------------------------------
+constexpr int kBwdBufs = 3;
+
+template <int D>
+struct SwzTile {
+  static constexpr int RB = D * 2, CPR = D / 8, DB = D / 32;
+  int voff[DB];  // this lane's transposing-read offsets (as the forward's V reads)
+  int roff;      // this lane's row-read base: row l32
+  int sw;        // v_swz of this lane's row
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int r = 4 * (g >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
+      voff[db] = r * RB + ((c ^ v_swz<D>(r)) << 4) + 8 * (i & 1);
+    }
+    roff = (lane & 31) * RB;
+    sw = v_swz<D>(lane & 31);
+  }
+  // 16 bytes of row l32, logical slot c
+  __device__ __forceinline__ int row(int c) const { return roff + ((c ^ sw) << 4); }
+};
+
+// acc^T[n][col] += sum_k Y[k][n] * M[k][col] over the 32 rows k of a swizzled
+// tile Y, M given as the packed 16-bit operand of a D-layout accumulator.
+template <class E, int D>
+__device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzTile<D>& sz,
+                                           const typename E::v8 (&m)[2], f32x16 (&acc)[D / 32]) {
+  using v4 = typename E::v4;
+  using v8 = typename E::v8;
+  constexpr int DB = D / 32, RB = D * 2, LA = FA_BWD_LOOKAHEAD;
+  v8 ring[LA + 1];
+#pragma unroll
+  for (int t = 0; t < 2 * DB + LA; ++t) {
+    if (t < 2 * DB) {
+      const unsigned char* b = tile + 16 * (t / DB) * RB + sz.voff[t % DB];
+      const v4 a0 = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)b));
+      const v4 a1 = __builtin_bit_cast(
+          v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
+      ring[t % (LA + 1)] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const int u = t - LA;
+    if (u >= 0) acc[u % DB] = E::mma(ring[u % (LA + 1)], m[u / DB], acc[u % DB]);
+  }
+}
+
+// S = X Y^T and dP = Z W^T over the head dim for one 32-row tile: X, Z rows
+// of swizzled LDS tiles (A operands), Y, W in registers (B operands); operand
+// reads issued FA_BWD_LOOKAHEAD steps ahead.
+template <class E, int D>
+__device__ __forceinline__ void two_products(const unsigned char* x, const unsigned char* z,
+                                             const SwzTile<D>& sz, int hi,
+                                             const typename E::v8 (&y)[D / 16],
+                                             const typename E::v8 (&w)[D / 16], f32x16& s,
+                                             f32x16& dp) {
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16, LA = FA_BWD_LOOKAHEAD;
+  v8 ra[LA + 1], rb[LA + 1];
+#pragma unroll
+  for (int t = 0; t < KS + LA; ++t) {
+    if (t < KS) {
+      ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
+      rb[t % (LA + 1)] = *(const v8*)(z + sz.row(2 * t + hi));
+    }
+    const int u = t - LA;
+    if (u >= 0) {
+      s = E::mma(ra[u % (LA + 1)], y[u], s);
+      dp = E::mma(rb[u % (LA + 1)], w[u], dp);
+    }
+  }
+}
+
+// Rows [32*t, 32*t + 32) of a head (cut at `limit` rows) into `dst`, slots
+// permuted by v_swz; each wave copies its share of the 1 KB blocks.
+template <int D>
+__device__ __forceinline__ void copy_rows_swz(const void* head, int t, int limit, unsigned char* dst,
+                                              int wave, int lane) {
+  constexpr int RB = D * 2, CPR = D / 8, NCP = 32 * RB / 1024;
+  static_assert(NCP % kBwdWaves == 0, "1 KB copies split evenly over the waves");
+  const auto rs = tile_rsrc(head, t, 32, limit, RB);
+#pragma unroll
+  for (int c = 0; c < NCP / kBwdWaves; ++c) {
+    const int blk = c * kBwdWaves + wave;
+    const int slot = blk * 64 + lane;
+    const int r = slot / CPR, ps = slot % CPR;
+    lds_copy16(rs, dst + blk * 1024, r * RB + ((ps ^ v_swz<D>(r)) << 4));
+  }
+}
+
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
+  constexpr int NCPW = TB / 1024 / kBwdWaves;  // copies per wave per tile and tensor
+  __shared__ __attribute__((aligned(1024))) unsigned char kb[kBwdBufs][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb[kBwdBufs][TB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int N = p.N;
+  const int bh = blockIdx.x / p.n_qt;
+  const int qt = p.n_qt - 1 - (blockIdx.x - bh * p.n_qt);
+  const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
+  int kl = N;
+  if (p.key_len != nullptr) {
+    const int x = p.key_len[b];
+    kl = x < 0 ? 0 : (x > N ? N : x);
+  }
+  kl = __builtin_amdgcn_readfirstlane(kl);
+  const int q_wg0 = qt * kBwdRows, qw0 = q_wg0 + 32 * wave, qrow = qw0 + l32;
+  int kv_end = kl;
+  if (CAUSAL) kv_end = min(kv_end, min(N, q_wg0 + kBwdRows));
+  const int nt = (kv_end + 31) / 32;
+  int w_end = CAUSAL ? min(kv_end, qw0 + 32) : kv_end;
+  if (qw0 >= N) w_end = 0;
+  const int wnt = (w_end + 31) / 32;
+  int wfull = kl / 32;
+  if (CAUSAL) wfull = min(wfull, (qw0 + 1) / 32);
+  wfull = min(wfull, wnt);
+
+  const size_t head = (size_t)bh * N * D, kv_head = (size_t)kvh * N * D;
+  const T* Kh = (const T*)p.k + kv_head;
+  const T* Vh = (const T*)p.v + kv_head;
+  v8 qf[KS], df[KS];
+  {
+    const auto rq = tile_rsrc((const T*)p.q + head, 0, N, N, D * 2);
+    const auto rd = tile_rsrc((const T*)p.dout + head, 0, N, N, D * 2);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      qf[st] = __builtin_bit_cast(v8, load16(rq, qrow * D * 2 + 32 * st + 16 * hi));
+      df[st] = __builtin_bit_cast(v8, load16(rd, qrow * D * 2 + 32 * st + 16 * hi));
+    }
+  }
+  const bool row_ok = qrow < N;
+  const float lse2 = row_ok ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
+  const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.0f;
+  const float c = p.c;
+  SwzTile<D> sz;
+  sz.init(pinned_int(lane));
+
+  auto copies = [&](int j, int buf) __attribute__((always_inline)) {
+    copy_rows_swz<D>(Kh, j, kv_end, kb[buf], wave, lane);
+    copy_rows_swz<D>(Vh, j, kv_end, vb[buf], wave, lane);
+  };
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  copies(0, 0);
+  copies(1, 1);
+  wait_vmem_keep<2 * NCPW>();  // tile 0 landed (tile 1 may be in flight)
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const int buf = j % kBwdBufs;
+    copies(j + 2, (j + 2) % kBwdBufs);  // past the end: empty ranges, nothing moves
+    auto tile = [&](auto masked) __attribute__((always_inline)) {
+      f32x16 s[1] = {f32x16{}};
+      f32x16 dp = {};
+      two_products<E, D>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
+      if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
+      v8 ds[2];
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * ps + e;
+          const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
+          ds[ps][e] = E::cvt(pr * (dp[i] - dl));
+        }
+      tr_product<E, D>(kb[buf], sz, ds, dq);
+    };
+    if (j < wfull) tile(std::false_type{});
+    else if (j < wnt) tile(std::true_type{});
+    wait_vmem_keep<2 * NCPW>();  // tile j+1 landed; tile j+2 may be in flight
+    __syncthreads();
+  }
+  wait_vmem();
+  if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
+}
+
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_dma(BwdParams p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
+  constexpr int NCPW = TB / 1024 / kBwdWaves;
+  __shared__ __attribute__((aligned(1024))) unsigned char qb[kBwdBufs][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char ob[kBwdBufs][TB];
+  __shared__ __attribute__((aligned(16))) float ls[kBwdBufs][32];
+  __shared__ __attribute__((aligned(16))) float dls[kBwdBufs][32];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int N = p.N;
+  const int kvh = blockIdx.x / p.n_kt;
+  const int kt = blockIdx.x - kvh * p.n_kt;
+  const int b = kvh / p.H_kv, g = kvh - b * p.H_kv;
+  int kl = N;
+  if (p.key_len != nullptr) {
+    const int x = p.key_len[b];
+    kl = x < 0 ? 0 : (x > N ? N : x);
+  }
+  kl = __builtin_amdgcn_readfirstlane(kl);
+  const int k_wg0 = kt * kBwdRows, kw0 = k_wg0 + 32 * wave, key = kw0 + l32;
+  const int nqt = (N + 31) / 32;
+  const int t_begin = CAUSAL ? k_wg0 / 32 : 0;
+  const int per_head = k_wg0 < kl ? nqt - t_begin : 0;
+  const int n_iter = per_head * p.group;
+  const bool wave_live = kw0 < kl;
+
+  const size_t kv_head = (size_t)kvh * N * D;
+  v8 kf[KS], vf[KS];
+  {
+    const auto rk = tile_rsrc((const T*)p.k + kv_head, 0, N, N, D * 2);
+    const auto rv = tile_rsrc((const T*)p.v + kv_head, 0, N, N, D * 2);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      kf[st] = __builtin_bit_cast(v8, load16(rk, key * D * 2 + 32 * st + 16 * hi));
+      vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
+    }
+  }
+  const float c = p.c;
+  SwzTile<D> sz;
+  sz.init(pinned_int(lane));
+
+  // iteration u: query head g*group + u / per_head, query tile t_begin + u % per_head
+  auto tile_of = [&](int u, int& t, size_t& qhead, int& lim) __attribute__((always_inline)) {
+    const int ph = max(per_head, 1);
+    const int hq = g * p.group + min(u / ph, p.group - 1);
+    t = t_begin + u % ph;
+    qhead = ((size_t)b * p.H + hq) * N;
+    lim = u < n_iter ? N : 0;
+  };
+  auto copies = [&](int u, int buf) __attribute__((always_inline)) {
+    int t, lim;
+    size_t qhead;
+    tile_of(u, t, qhead, lim);
+    copy_rows_swz<D>((const T*)p.q + qhead * D, t, lim, qb[buf], wave, lane);
+    copy_rows_swz<D>((const T*)p.dout + qhead * D, t, lim, ob[buf], wave, lane);
+  };
+  float lreg = INFINITY, dlreg = 0.0f;
+  auto row_stats = [&](int u) __attribute__((always_inline)) {
+    if (tid < 32) {
+      int t, lim;
+      size_t qhead;
+      tile_of(u, t, qhead, lim);
+      const int row = 32 * t + tid;
+      const bool ok = row < lim;
+      lreg = ok ? p.lse2[qhead + row] : INFINITY;
+      dlreg = ok ? p.delta[qhead + row] : 0.0f;
+    }
+  };
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dk[db] = f32x16{}, dv[db] = f32x16{};
+  if (n_iter > 0) {
+    row_stats(0);
+    copies(0, 0);
+    copies(1, 1);
+    wait_vmem_keep<2 * NCPW>();
+    if (tid < 32) ls[0][tid] = lreg, dls[0][tid] = dlreg;
+  }
+  __syncthreads();
+  for (int u = 0; u < n_iter; ++u) {
+    const int buf = u % kBwdBufs, nbuf = (u + 1) % kBwdBufs;
+    int t, lim;
+    size_t qhead;
+    tile_of(u, t, qhead, lim);
+    row_stats(u + 1);
+    copies(u + 2, (u + 2) % kBwdBufs);
+    if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
+      f32x16 s = {}, dp = {};
+      two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
+      v8 pf[2], dsf[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *(const f32x4*)(&ls[buf][8 * q4 + 4 * hi]);
+        const f32x4 d4 = *(const f32x4*)(&dls[buf][8 * q4 + 4 * hi]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          const int qry = 32 * t + 8 * q4 + 4 * hi + e;
+          const bool ok = key < kl && (!CAUSAL || key <= qry);
+          const float pr = ok ? fast_exp2(fmaf(s[i], c, -l4[e])) : 0.0f;
+          pf[i >> 3][i & 7] = E::cvt(pr);
+          dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
+        }
+      }
+      tr_product<E, D>(ob[buf], sz, pf, dv);
+      tr_product<E, D>(qb[buf], sz, dsf, dk);
+    }
+    wait_vmem_keep<2 * NCPW>();  // row stats u+1 and tile u+1 landed; tile u+2 may be in flight
+    if (tid < 32) ls[nbuf][tid] = lreg, dls[nbuf][tid] = dlreg;
+    __syncthreads();
+  }
+  wait_vmem();
+  if (key < N) {
+    store_grad<T, DB>((T*)p.dk + kv_head + (size_t)key * D, hi, p.scale, dk);
+    store_grad<T, DB>((T*)p.dv + kv_head + (size_t)key * D, hi, 1.0f, dv);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch table
 // ---------------------------------------------------------------------------
 constexpr int kWaves = FA_WAVES;  // x 32 query rows per workgroup
@@ -2243,11 +2566,16 @@ hipError_t launch_backward_t(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipLaunchKernel((const void*)attn_bwd_prep<typename E::T, D>, dim3((unsigned)g_prep),
                                  dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel((const void*)attn_bwd_dq<E, D, C>, dim3((unsigned)g_dq), dim3(kBwdWaves * 64),
-                      args, 0, stream);
+#if FA_BWD_DMA
+  const void* kdq = (const void*)attn_bwd_dq_dma<E, D, C>;
+  const void* kkv = (const void*)attn_bwd_dkdv_dma<E, D, C>;
+#else
+  const void* kdq = (const void*)attn_bwd_dq<E, D, C>;
+  const void* kkv = (const void*)attn_bwd_dkdv<E, D, C>;
+#endif
+  e = hipLaunchKernel(kdq, dim3((unsigned)g_dq), dim3(kBwdWaves * 64), args, 0, stream);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)attn_bwd_dkdv<E, D, C>, dim3((unsigned)g_kv),
-                         dim3(kBwdWaves * 64), args, 0, stream);
+  return hipLaunchKernel(kkv, dim3((unsigned)g_kv), dim3(kBwdWaves * 64), args, 0, stream);
 }
 template <class E>
 hipError_t launch_backward_e(int d, bool causal, const BwdParams& p, hipStream_t s) {
