@@ -1803,6 +1803,9 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 #ifndef FA_BWD_DMA
 #define FA_BWD_DMA 1  // backward passes on direct-to-LDS copies (0: register-staged tiles)
 #endif
+#ifndef FA_BWD_SPLIT
+#define FA_BWD_SPLIT 0  // 1: dV and dK in separate passes (each recomputes S)
+#endif
 #ifndef FA_BWD_KV_OCC
 #define FA_BWD_KV_OCC 2  // waves per SIMD the dK/dV pass is compiled for (1: 512 registers)
 #endif
@@ -2164,6 +2167,21 @@ __device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzT
   }
 }
 
+// S = X Y^T alone (as two_products without the second product).
+template <class E, int D>
+__device__ __forceinline__ void one_product(const unsigned char* x, const SwzTile<D>& sz, int hi,
+                                            const typename E::v8 (&y)[D / 16], f32x16& s) {
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16, LA = FA_BWD_LOOKAHEAD;
+  v8 ra[LA + 1];
+#pragma unroll
+  for (int t = 0; t < KS + LA; ++t) {
+    if (t < KS) ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
+    const int u = t - LA;
+    if (u >= 0) s = E::mma(ra[u % (LA + 1)], y[u], s);
+  }
+}
+
 // S = X Y^T and dP = Z W^T over the head dim for one 32-row tile: X, Z rows
 // of swizzled LDS tiles (A operands), Y, W in registers (B operands); operand
 // reads issued FA_BWD_LOOKAHEAD steps ahead.
@@ -2299,7 +2317,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
 }
 
-template <class E, int D, bool CAUSAL>
+// MODE 0: dK and dV in one pass; 1: dV only; 2: dK only (S recomputed by both).
+template <class E, int D, bool CAUSAL, int MODE = 0>
 __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_dma(BwdParams p) {
   using T = typename E::T;
   using v8 = typename E::v8;
@@ -2338,7 +2357,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       kf[st] = __builtin_bit_cast(v8, load16(rk, key * D * 2 + 32 * st + 16 * hi));
-      vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
+      if constexpr (MODE != 1) vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
     }
   }
   const float c = p.c;
@@ -2393,7 +2412,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     copies(u + 2, (u + 2) % kBwdBufs);
     if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
       f32x16 s = {}, dp = {};
-      two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
+      if constexpr (MODE == 1) one_product<E, D>(qb[buf], sz, hi, kf, s);
+      else two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
       v8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -2406,11 +2426,11 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
           const bool ok = key < kl && (!CAUSAL || key <= qry);
           const float pr = ok ? fast_exp2(fmaf(s[i], c, -l4[e])) : 0.0f;
           pf[i >> 3][i & 7] = E::cvt(pr);
-          dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
+          if constexpr (MODE != 1) dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
         }
       }
-      tr_product<E, D>(ob[buf], sz, pf, dv);
-      tr_product<E, D>(qb[buf], sz, dsf, dk);
+      if constexpr (MODE != 2) tr_product<E, D>(ob[buf], sz, pf, dv);
+      if constexpr (MODE != 1) tr_product<E, D>(qb[buf], sz, dsf, dk);
     }
     wait_vmem_keep<2 * NCPW>();  // row stats u+1 and tile u+1 landed; tile u+2 may be in flight
     if (tid < 32) ls[nbuf][tid] = lreg, dls[nbuf][tid] = dlreg;
@@ -2418,8 +2438,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   }
   wait_vmem();
   if (key < N) {
-    store_grad<T, DB>((T*)p.dk + kv_head + (size_t)key * D, hi, p.scale, dk);
-    store_grad<T, DB>((T*)p.dv + kv_head + (size_t)key * D, hi, 1.0f, dv);
+    if constexpr (MODE != 1) store_grad<T, DB>((T*)p.dk + kv_head + (size_t)key * D, hi, p.scale, dk);
+    if constexpr (MODE != 2) store_grad<T, DB>((T*)p.dv + kv_head + (size_t)key * D, hi, 1.0f, dv);
   }
 }
 
@@ -2575,6 +2595,13 @@ hipError_t launch_backward_t(const BwdParams& p, hipStream_t stream) {
 #endif
   e = hipLaunchKernel(kdq, dim3((unsigned)g_dq), dim3(kBwdWaves * 64), args, 0, stream);
   if (e != hipSuccess) return e;
+#if FA_BWD_DMA && FA_BWD_SPLIT
+  // dV and dK in passes of their own: one accumulator set each
+  e = hipLaunchKernel((const void*)attn_bwd_dkdv_dma<E, D, C, 1>, dim3((unsigned)g_kv),
+                      dim3(kBwdWaves * 64), args, 0, stream);
+  if (e != hipSuccess) return e;
+  kkv = (const void*)attn_bwd_dkdv_dma<E, D, C, 2>;
+#endif
   return hipLaunchKernel(kkv, dim3((unsigned)g_kv), dim3(kBwdWaves * 64), args, 0, stream);
 }
 template <class E>
