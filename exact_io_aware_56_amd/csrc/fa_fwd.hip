@@ -1771,6 +1771,8 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
   float L = 0.0f;
   if (mx > -INFINITY) {
     const float* wo = p.ws_o + row * p.S * D;
+    // unrolled so that several chunks' loads are in flight at once
+#pragma unroll 4
     for (int s = 0; s < p.S; ++s) {
       const float w = expf(ls[s] - mx);  // 0 for an empty chunk
       L += w;
