@@ -99,6 +99,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_PIPE_IGLP
 #define FA_PIPE_IGLP 3  // pipelined kernel: the compiler's MFMA/exp interleave for each half-step (-1: none)
 #endif
+#ifndef FA_PIPE_PREFETCH
+#define FA_PIPE_PREFETCH 0  // pipelined kernel: next causal item's Q and first tiles under the epilogue
+#endif
 #ifndef FA_PIPE_NBUF
 #define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
 #endif
@@ -1042,6 +1045,10 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char v2s[TB2];
   __shared__ __attribute__((aligned(1024))) unsigned char v3s[TB3];
+  // With the cross-item prefetch the next item's first tiles land in the K/V
+  // buffers while this item's O is staged, so O gets a region of its own.
+  constexpr bool PF = FA_PIPE_PREFETCH && CAUSAL && !F8;
+  __shared__ __attribute__((aligned(1024))) unsigned char ostage[PF ? NW * G * 32 * D * 2 : 16];
   auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* {
     return i == 0 ? k0s : i == 1 ? k1s : i == 2 ? k2s : k3s;
   };
@@ -1054,8 +1061,32 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = p.N;
 
-  // One query tile of one head, start to finish.
-  auto process = [&](int bh, int qt) __attribute__((always_inline)) {
+  // Q^T operand: lane holds its query row's head-dim elements
+  // [16*st + 8*hi, +8) (16-bit) or [64*st + 32*hi, +32) (fp8).
+  QT qf[G][KS];
+  auto load_q = [&](const RowRange& r) __attribute__((always_inline)) {
+    const size_t qhead = (size_t)r.bh * N * D;
+    const auto rq = tile_rsrc((const unsigned char*)p.q + qhead * (KRB / D), r.q_wg0 / BR, BR, N, KRB);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int row = r.qrow + 32 * g - r.q_wg0;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (F8) {
+          const int off = row * KRB + 64 * s + 32 * hi;
+          qf[g][s] = __builtin_shufflevector(load16(rq, off), load16(rq, off + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          qf[g][s] = __builtin_bit_cast(v8, load16(rq, row * KRB + 32 * s + 16 * hi));
+        }
+      }
+    }
+  };
+
+  // One query tile of one head, start to finish. With the prefetch, an item
+  // that follows another finds its Q and first K/V tiles already issued, and
+  // issues those of the item after it (nbh, nqt) before its own epilogue.
+  auto process = [&](int bh, int qt, bool prefetched, bool has_next, int nbh, int nqt)
+      __attribute__((always_inline)) {
   // Lane-derived offsets are recomputed per tile from an opaque copy of the
   // lane index, so that they are not kept live (and spilled) across tiles.
   const int ln = pinned_int(lane);
@@ -1088,25 +1119,8 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   const unsigned char* Kh = (const unsigned char*)p.k + kv_head * (KRB / D);
   const unsigned char* Vh = (const unsigned char*)p.v + kv_head * (KRB / D);
 
-  // Q^T operand: lane holds its query row's head-dim elements
-  // [16*st + 8*hi, +8) (16-bit) or [64*st + 32*hi, +32) (fp8).
-  QT qf[G][KS];
-  {
-    const auto rq = tile_rsrc(Qh, rr.q_wg0 / BR, BR, N, KRB);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int row = rr.qrow + 32 * g - rr.q_wg0;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if constexpr (F8) {
-          const int off = row * KRB + 64 * s + 32 * hi;
-          qf[g][s] = __builtin_shufflevector(load16(rq, off), load16(rq, off + 16), 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-          qf[g][s] = __builtin_bit_cast(v8, load16(rq, row * KRB + 32 * s + 16 * hi));
-        }
-      }
-    }
-  }
+  (void)Qh;
+  if (!(PF && prefetched)) load_q(rr);
   // One buffer resource per operand over the head's first kl key rows (the
   // host keeps a head under 1 GiB): a tile's copy only adds its byte offset,
   // and rows at or beyond kl (a ragged last tile, tiles past the end) read
@@ -1115,6 +1129,21 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   const auto rsV = buffer_rsrc(Vh, rr.kl * KRB);
   // K tile j (and V tile j for 16-bit inputs) straight into LDS, 16-byte
   // slots permuted per row as the operand reads expect.
+  auto copy_tile_with = [&](__amdgpu_buffer_rsrc_t rs, int j, unsigned char* dst, auto is_v)
+      __attribute__((always_inline)) {
+    constexpr bool IV = decltype(is_v)::value;
+    constexpr int cpr = IV ? CPR : KCPR, rb = IV ? RB : KRB;
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) {
+      const int blk = c * NW + wave;
+      if (NKC % NW == 0 || blk < NKC) {
+        const int slot = blk * 64 + lane;
+        const int r = slot / cpr, ps = slot % cpr;
+        const int lc = ps ^ (IV ? v_swz<D>(r) : F8 ? k8_swz<D>(r) : k_swz<D>(r));
+        lds_copy16(rs, dst + blk * 1024, j * (BC * rb) + r * rb + (lc << 4));
+      }
+    }
+  };
   auto copy_tile = [&](int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
     constexpr bool IV = decltype(is_v)::value;
     constexpr int cpr = IV ? CPR : KCPR, rb = IV ? RB : KRB;
@@ -1297,15 +1326,17 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
     __syncthreads();
   };
 
-  copy_tile(0, k0s, std::false_type{});
+  if (!(PF && prefetched)) {
+    copy_tile(0, k0s, std::false_type{});
 #pragma unroll
-  for (int j = 1; j < NB; ++j) {
-    copy_tile(j, kbuf(j), std::false_type{});
-    if constexpr (F8) {
-      vload(j - 1);
-      vstore(vbuf(j - 1));
-    } else {
-      copy_tile(j - 1, vbuf(j - 1), std::true_type{});
+    for (int j = 1; j < NB; ++j) {
+      copy_tile(j, kbuf(j), std::false_type{});
+      if constexpr (F8) {
+        vload(j - 1);
+        vstore(vbuf(j - 1));
+      } else {
+        copy_tile(j - 1, vbuf(j - 1), std::true_type{});
+      }
     }
   }
   wait_vmem_keep<KEEP>();
@@ -1351,15 +1382,35 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // now stage O (8 KB per wave for D = 128, two waves per buffer).
   wait_vmem();
   __syncthreads();
+  if constexpr (PF) {
+    if (has_next) {
+      // The next item's Q and first tiles, issued now that every wave is done
+      // with the K/V buffers; they land while this item's O is written.
+      const RowRange rn = row_range_at<BR, BC, CAUSAL, WR>(p, nbh, nqt, wave, l32);
+      load_q(rn);
+      const size_t nkv = (size_t)rn.kv_bh * N * D;
+      const auto nK = buffer_rsrc((const unsigned char*)p.k + nkv * (KRB / D), rn.kl * KRB);
+      const auto nV = buffer_rsrc((const unsigned char*)p.v + nkv * (KRB / D), rn.kl * KRB);
+      copy_tile_with(nK, 0, k0s, std::false_type{});
+#pragma unroll
+      for (int j = 1; j < NB; ++j) {
+        copy_tile_with(nK, j, kbuf(j), std::false_type{});
+        copy_tile_with(nV, j - 1, vbuf(j - 1), std::true_type{});
+      }
+    }
+  }
   static_assert(NW * G <= 8 && TB >= 2 * 32 * D * 2, "O staging space");
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int slot = wave * G + g;
-    unsigned char* stage = (slot < 2 ? k0s : slot < 4 ? k1s : slot < 6 ? v0s : v1s) +
-                           (slot & 1) * (32 * D * 2);
+    unsigned char* stage = PF ? ostage + slot * (32 * D * 2)
+                              : (slot < 2 ? k0s : slot < 4 ? k1s : slot < 6 ? v0s : v1s) +
+                                    (slot & 1) * (32 * D * 2);
     epilogue_staged<T, D, DB>(p, rr.bh, rr.qw0 + 32 * g, lane, m[g], l[g], o[g], stage);
   }
-  __syncthreads();  // staging reads done before the next tile's copies land
+  // staging reads done before the next tile's copies land (a region of its
+  // own with the prefetch: each wave only ever reuses its own slice)
+  if constexpr (!PF) __syncthreads();
   };
 
   // Causal work is folded: a workgroup takes query tile n_qt-1-u and then
@@ -1375,7 +1426,8 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   const int bh = logical / units, u = logical - bh * units;
   const int items = CAUSAL && u != p.n_qt - 1 - u ? 2 : 1;
 #pragma nounroll
-  for (int it = 0; it < items; ++it) process(bh, CAUSAL && it == 0 ? p.n_qt - 1 - u : u);
+  for (int it = 0; it < items; ++it)
+    process(bh, CAUSAL && it == 0 ? p.n_qt - 1 - u : u, it > 0, it + 1 < items, bh, u);
 }
 
 // ---------------------------------------------------------------------------
