@@ -13,6 +13,7 @@ Every function here is pinned by tests that do not reuse its own formulas
 closed forms and invariants); none is "parity unpinned".
 """
 from .attention import (attention_forward, attention_rows, attention_decode,  # noqa: F401
+                        attention_varlen, attention_varlen_rows, packed_segments,
                         probabilities,
                         masked_scores, softmax_stats, allowed_mask, clamp_key_len)
 from .online import online_forward  # noqa: F401

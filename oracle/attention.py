@@ -175,6 +175,64 @@ def attention_decode(q, k, v, scale: float, causal: bool = False,
     return o, lse
 
 
+def packed_segments(cu_seqlens, T: int, max_seqlen: Optional[int] = None):
+    """(start, length) of each sequence of a packed batch of T rows.
+
+    Sequence b holds rows [cu[b], cu[b+1]); bounds are clamped to [0, T] with the
+    end no earlier than the start, and a length above max_seqlen (when given) is
+    cut to max_seqlen.
+    """
+    cu = [int(x) for x in cu_seqlens]
+    out = []
+    for b in range(len(cu) - 1):
+        s0 = min(max(cu[b], 0), T)
+        s1 = min(max(cu[b + 1], s0), T)
+        n = s1 - s0 if max_seqlen is None else min(s1 - s0, int(max_seqlen))
+        out.append((s0, n))
+    return out
+
+
+def attention_varlen(q, k, v, cu_seqlens, scale: float, causal: bool = False,
+                     max_seqlen: Optional[int] = None, row_block: int = 2048):
+    """O [H,T,d] and LSE [H,T] (float64) of a packed variable-length batch.
+
+    Packed batches of sequences of unequal length are among the richer masks
+    named through the FlashMask title in the bibliography of FlashAttention
+    (ES); the pages do not define them further. Reading: q is [H, T, d] and k, v
+    are [H_kv, T, d]; the sequences are concatenated along the row axis, sequence
+    b occupying rows [cu[b], cu[b+1]) of every head (packed_segments), and each
+    sequence is attended on its own: row i of sequence b sees exactly the keys of
+    sequence b (and, when causal, only those at or before its own position).
+    That is the plain forward applied to each sequence as one batch entry, which
+    is how it is computed here. K/V heads are grouped as in attention_forward.
+    Rows that belong to no sequence are not defined and come back as NaN.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    H, T, d = q.shape
+    H_kv = k.shape[0]
+    o = np.full((H, T, v.shape[-1]), np.nan)
+    lse = np.full((H, T), np.nan)
+    for s0, n in packed_segments(cu_seqlens, T, max_seqlen):
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            for r0 in range(0, n, row_block):
+                rows = np.arange(r0, min(n, r0 + row_block))
+                o[h, s0 + rows], lse[h, s0 + rows] = _rows_forward(
+                    q[h, s0 + rows], k[g, s0:s0 + n], v[g, s0:s0 + n], scale, rows, causal, n)
+    return o, lse
+
+
+def attention_varlen_rows(q, k, v, cu_seqlens, scale: float, causal: bool, b: int, h: int,
+                          rows: Sequence[int], max_seqlen: Optional[int] = None):
+    """O and LSE of selected rows (positions within sequence b) of query head h
+    of a packed batch, each against its whole sequence."""
+    rows = np.asarray(rows, dtype=np.int64)
+    s0, n = packed_segments(cu_seqlens, q.shape[1], max_seqlen)[b]
+    g = kv_head(h, q.shape[0], k.shape[0])
+    return _rows_forward(_as64(q[h, s0 + rows]), _as64(k[g, s0:s0 + n]), _as64(v[g, s0:s0 + n]),
+                         scale, rows, causal, n)
+
+
 def probabilities(q, k, scale: float, causal: bool, key_len, b: int, h: int):
     """The full N x N probability matrix P of one (b, h), for checks on P itself."""
     N = q.shape[2]

@@ -550,3 +550,140 @@ def test_window_matches_torch_sdpa_band_mask():
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=0.25)
     assert np.abs(O - ref.numpy()).max() <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches
+
+def segment_ids(cu, T):
+    """Sequence index of every packed row (-1 for rows in no sequence)."""
+    seg = np.full(T, -1)
+    for b in range(len(cu) - 1):
+        seg[cu[b]:cu[b + 1]] = b
+    return seg
+
+
+def brute_force_packed(q, k, v, cu, scale, causal):
+    """Naive exp(s)/sum(exp(s)) over the whole packed row axis, 50 digits:
+    packed row i sees packed row j iff both lie in one sequence (and j <= i
+    when causal)."""
+    H, T, d = q.shape
+    group = H // k.shape[0]
+    seg = segment_ids(cu, T)
+    O = np.full((H, T, d), np.nan)
+    L = np.full((H, T), np.nan)
+    for h in range(H):
+        g = h // group
+        for i in range(T):
+            if seg[i] < 0:
+                continue
+            allowed = [j for j in range(T) if seg[j] == seg[i] and (not causal or j <= i)]
+            w = {j: mpmath.exp(mpmath.mpf(scale) * mpmath.fsum(
+                mpmath.mpf(float(q[h, i, t])) * mpmath.mpf(float(k[g, j, t])) for t in range(d)))
+                for j in allowed}
+            z = mpmath.fsum(w.values())
+            for t in range(d):
+                O[h, i, t] = float(mpmath.fsum(w[j] * mpmath.mpf(float(v[g, j, t]))
+                                               for j in allowed) / z)
+            L[h, i] = float(mpmath.log(z))
+    return O, L
+
+
+PACKED = [([0, 5, 5, 6, 14], 2, 1), ([0, 16], 1, 1), ([0, 3, 9, 12], 4, 2), ([2, 7, 13], 2, 2)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cu,H,H_kv", PACKED)
+def test_packed_matches_brute_force(cu, H, H_kv, causal):
+    rng = np.random.default_rng(80 + len(cu) + H + causal)
+    T, d = 16, 4
+    q = rng.standard_normal((H, T, d))
+    k = rng.standard_normal((H_kv, T, d))
+    v = rng.standard_normal((H_kv, T, d))
+    O, L = oracle.attention_varlen(q, k, v, cu, 0.5, causal)
+    O2, L2 = brute_force_packed(q, k, v, cu, 0.5, causal)
+    assert np.array_equal(np.isnan(O), np.isnan(O2)) and np.array_equal(np.isnan(L), np.isnan(L2))
+    ok = ~np.isnan(L2)
+    assert np.abs(O[~np.isnan(O2)] - O2[~np.isnan(O2)]).max() <= 1e-13
+    assert np.abs(L[ok] - L2[ok]).max() <= 1e-13
+
+
+def test_packed_matches_torch_sdpa_block_diagonal_mask():
+    rng = np.random.default_rng(83)
+    cu = [0, 37, 38, 100, 161]
+    H, H_kv, T, d = 4, 2, 161, 16
+    q = rng.standard_normal((H, T, d))
+    k = rng.standard_normal((H_kv, T, d))
+    v = rng.standard_normal((H_kv, T, d))
+    seg = torch.as_tensor(segment_ids(cu, T))
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    for causal in (False, True):
+        O, L = oracle.attention_varlen(q, k, v, cu, 0.3, causal)
+        mask = (seg[:, None] == seg[None, :]) & ((j <= i) if causal else True)
+        kk = torch.from_numpy(np.repeat(k, 2, axis=0))
+        vv = torch.from_numpy(np.repeat(v, 2, axis=0))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], kk[None], vv[None], attn_mask=mask, scale=0.3)[0]
+        assert np.abs(O - ref.numpy()).max() <= 1e-12
+
+
+def test_packed_equals_padded_batch_with_key_lengths():
+    # The same sequences laid out padded ([B, H, n_max, d], garbage past each
+    # length, key_len = lengths) through the padded forward: the valid rows agree.
+    rng = np.random.default_rng(84)
+    lens = [9, 1, 30, 17]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    H, T, d, n_max = 3, int(cu[-1]), 8, max(lens)
+    q = rng.standard_normal((H, T, d))
+    k = rng.standard_normal((H, T, d))
+    v = rng.standard_normal((H, T, d))
+    for causal in (False, True):
+        O, L = oracle.attention_varlen(q, k, v, cu, 0.4, causal)
+        pad = [rng.standard_normal((len(lens), H, n_max, d)) * 50 for _ in range(3)]
+        for b, n in enumerate(lens):
+            for x, y in zip(pad, (q, k, v)):
+                x[b, :, :n] = y[:, cu[b]:cu[b] + n]
+        Op, Lp = oracle.attention_forward(*pad, 0.4, causal, key_len=np.array(lens))
+        for b, n in enumerate(lens):
+            assert np.abs(O[:, cu[b]:cu[b] + n] - Op[b, :, :n]).max() <= 1e-13
+            assert np.abs(L[:, cu[b]:cu[b] + n] - Lp[b, :, :n]).max() <= 1e-13
+
+
+def test_packed_uncovered_rows_clamping_and_max_seqlen():
+    rng = np.random.default_rng(85)
+    q, k, v = (rng.standard_normal((2, 12, 4)) for _ in range(3))
+    O, L = oracle.attention_varlen(q, k, v, [1, 4, 4, 9], 0.5, True)
+    assert np.isnan(L[:, [0, 9, 10, 11]]).all() and not np.isnan(L[:, 1:9]).any()
+    # causal first row of a sequence sees only itself
+    assert np.abs(O[:, 1] - v[:, 1]).max() <= 1e-15 and np.abs(O[:, 4] - v[:, 4]).max() <= 1e-15
+    # bounds past T are clamped, a decreasing end gives an empty sequence
+    assert oracle.packed_segments([0, 5, 3, 40], 12) == [(0, 5), (5, 0), (3, 9)]
+    # max_seqlen cuts a sequence to its first rows, which keep their values
+    O2, L2 = oracle.attention_varlen(q, k, v, [1, 4, 4, 9], 0.5, True, max_seqlen=3)
+    assert np.isnan(L2[:, 7:9]).all()
+    assert np.array_equal(O2[:, 4:7], O[:, 4:7]) and np.array_equal(L2[:, 1:7], L[:, 1:7])
+
+
+def test_packed_rows_api_matches_full():
+    rng = np.random.default_rng(86)
+    cu = [0, 20, 57]
+    q = rng.standard_normal((4, 57, 8))
+    k, v = (rng.standard_normal((2, 57, 8)) for _ in range(2))
+    O, L = oracle.attention_varlen(q, k, v, cu, 0.5, True)
+    rows = [0, 5, 36]
+    o, lse = oracle.attention_varlen_rows(q, k, v, cu, 0.5, True, 1, 3, rows)
+    assert np.array_equal(o, O[3, 20 + np.array(rows)]) and np.array_equal(lse, L[3, 20 + np.array(rows)])
+
+
+def test_pins_catch_planted_segment_mistake(monkeypatch):
+    # A sequence that reaches one row past its end must fail the brute force.
+    orig = oatt.packed_segments
+    monkeypatch.setattr(oatt, "packed_segments",
+                        lambda cu, T, m=None: [(s, min(n + 1, T - s)) for s, n in orig(cu, T, m)])
+    rng = np.random.default_rng(87)
+    q, k, v = (rng.standard_normal((1, 16, 4)) for _ in range(3))
+    cu = [0, 3, 9, 16]
+    O, _ = oracle.attention_varlen(q, k, v, cu, 0.5, False)
+    O2, _ = brute_force_packed(q, k, v, cu, 0.5, False)
+    assert np.abs(O - O2).max() > 1e-3

@@ -19,6 +19,11 @@ Recipe (the same for every workload):
 * Storage cast: bf16 / fp16 by round-to-nearest-even (torch's ``Tensor.to``);
   fp32 unchanged; fp8 e4m3 (OCP "fn" variant) by per-tensor quantisation with
   ``s = amax(|x|) / 448`` (float32) and ``x_q = e4m3(RNE(clamp(x / s, ±448)))``.
+* Packed variable-length batches: the B sequence lengths
+  ``rng.integers(lo, hi + 1, size=B)`` are drawn first, then Q of shape
+  ``[H, T, d]`` and K, V of shape ``[H_kv, T, d]`` (T = the sum of the lengths;
+  the sequences are concatenated along the row axis, ``cu_seqlens`` holds their
+  bounds), then the outliers per K/V head over all T rows, then the cast.
 
 ``Workload.exact()`` returns the float64 values the stored tensors represent
 (for fp8: ``float64(x_q) * float64(s)``); that is what the oracle must consume.
@@ -62,6 +67,7 @@ class Spec:
     H_kv: Optional[int] = None  # K/V heads (None: H, no grouping)
     Nq: Optional[int] = None    # decode: queries per head against N cached keys
     window_left: int = -1       # causal sliding window: keys j >= i - window_left
+    packed: bool = False        # B sequences of lengths in key_len_range, concatenated
 
     @property
     def is_decode(self) -> bool:
@@ -75,9 +81,13 @@ class Spec:
     def kv_heads(self) -> int:
         return self.H if self.H_kv is None else self.H_kv
 
-    def flops(self) -> float:
+    def flops(self, lengths=None) -> float:
         """Nominal attention FLOP: 4*B*H*N^2*d, halved when causal; decode:
-        4*B*H*Nq*N*d (every query against the whole cache)."""
+        4*B*H*Nq*N*d (every query against the whole cache); packed batches:
+        4*H*d*sum(n_b^2) over the drawn sequence lengths, halved when causal."""
+        if self.packed:
+            f = 4.0 * self.H * self.d * float(np.sum(np.asarray(lengths, np.float64) ** 2))
+            return f / 2 if self.causal else f
         if self.is_decode:
             return 4.0 * self.B * self.H * self.Nq * self.N * self.d
         if self.window_left >= 0 and self.causal:
@@ -85,8 +95,11 @@ class Spec:
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
-    def exps(self) -> float:
+    def exps(self, lengths=None) -> float:
         """Nominal exponentials (one per score): B*H*N^2, halved when causal."""
+        if self.packed:
+            e = float(self.H) * float(np.sum(np.asarray(lengths, np.float64) ** 2))
+            return e / 2 if self.causal else e
         if self.is_decode:
             return float(self.B) * self.H * self.Nq * self.N
         if self.window_left >= 0 and self.causal:
@@ -129,6 +142,11 @@ SPECS = {
     "long_causal_window_bf16": Spec("long_causal_window_bf16", 1, 32, 8192, 128, "bf16", True,
                                     1.0 / math.sqrt(128), outlier_frac=0.01, seed=20260009,
                                     window_left=1023),
+    # A packed training batch of the long causal decoder's heads: 16 sequences of
+    # 256..8192 tokens concatenated along the row axis (49,314 rows).
+    "packed_causal_bf16": Spec("packed_causal_bf16", 16, 32, 8192, 128, "bf16", True,
+                               1.0 / math.sqrt(128), key_len_range=(256, 8192),
+                               outlier_frac=0.01, seed=20260010, packed=True),
     # One new token per sequence against a 16K-key cache: 16 sequences whose
     # caches hold 8K..16K valid keys, 32 query heads over 8 K/V heads.
     "decode_grouped_bf16": Spec("decode_grouped_bf16", 16, 32, 16384, 128, "bf16", True,
@@ -147,6 +165,17 @@ class Workload:
     key_len: Optional[np.ndarray]  # int32 [B] or None
     descale: Tuple[float, float, float]  # (q, k, v); 1.0 unless fp8
     outlier_rows: Optional[np.ndarray] = None  # int64 [B,H_kv,n_out]
+    cu_seqlens: Optional[np.ndarray] = None  # packed: int32 [B+1] sequence bounds
+
+    @property
+    def lengths(self) -> Optional[np.ndarray]:
+        return None if self.cu_seqlens is None else np.diff(self.cu_seqlens)
+
+    def flops(self) -> float:
+        return self.spec.flops(self.lengths)
+
+    def exps(self) -> float:
+        return self.spec.exps(self.lengths)
 
     def exact(self):
         """float64 arrays (q, k, v) holding exactly the values the storage represents."""
@@ -172,6 +201,8 @@ def _quantise_fp8(x: np.ndarray):
 def draw(spec: Spec, seed: Optional[int] = None) -> Workload:
     """Generate the workload for ``spec`` (seed defaults to the spec's own)."""
     rng = np.random.default_rng(spec.seed if seed is None else seed)
+    if spec.packed:
+        return _draw_packed(spec, rng)
     shape = (spec.B, spec.H, spec.q_len, spec.d)
     kv_shape = (spec.B, spec.kv_heads, spec.N, spec.d)
     q = rng.standard_normal(shape).astype(np.float32)
@@ -199,6 +230,29 @@ def draw(spec: Spec, seed: Optional[int] = None) -> Workload:
         descale = (1.0, 1.0, 1.0)
     return Workload(spec, qt.contiguous(), kt.contiguous(), vt.contiguous(), key_len,
                     descale, rows)
+
+
+def _draw_packed(spec: Spec, rng) -> Workload:
+    lo, hi = spec.key_len_range
+    lens = rng.integers(lo, hi + 1, size=spec.B)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = rng.standard_normal((spec.H, T, spec.d)).astype(np.float32)
+    k = rng.standard_normal((spec.kv_heads, T, spec.d)).astype(np.float32)
+    v = rng.standard_normal((spec.kv_heads, T, spec.d)).astype(np.float32)
+    rows = None
+    if spec.outlier_frac > 0:
+        n_out = int(round(spec.outlier_frac * T))
+        rows = np.zeros((1, spec.kv_heads, n_out), dtype=np.int64)
+        for h in range(spec.kv_heads):
+            idx = rng.choice(T, n_out, replace=False)
+            rows[0, h] = idx
+            k[h, idx, :] *= np.float32(spec.outlier_scale)
+    if spec.dtype not in ("bf16", "fp16"):
+        raise ValueError("packed workloads are 16-bit")
+    tdt = TORCH_STORAGE[spec.dtype]
+    qt, kt, vt = (torch.from_numpy(x).to(tdt).contiguous() for x in (q, k, v))
+    return Workload(spec, qt, kt, vt, None, (1.0, 1.0, 1.0), rows, cu)
 
 
 def spec(name: str) -> Spec:
