@@ -74,13 +74,14 @@ def decode_bytes(spec, key_len) -> int:
     return 2 * e * spec.kv_heads * spec.d * kl + qo + 4 * spec.B * spec.H * spec.Nq
 
 
-def algorithmic_bytes(spec) -> int:
+def algorithmic_bytes(spec, rows=None) -> int:
     """Q, K, V read once, O written once, LSE written once (K and V have
-    H_kv heads when the workload groups them)."""
+    H_kv heads when the workload groups them). `rows`: query rows per head
+    (the packed rows of a packed batch; B*N otherwise)."""
     e_in = {"fp32": 4, "fp16": 2, "bf16": 2, "fp8": 1}[spec.dtype]
     e_out = {"fp32": 4, "fp16": 2, "bf16": 2, "fp8": 2}[spec.dtype]
-    row = spec.B * spec.N * spec.d
-    return ((e_in + e_out) * spec.H + 2 * e_in * spec.kv_heads) * row + 4 * spec.B * spec.H * spec.N
+    rows = spec.B * spec.N if rows is None else rows
+    return ((e_in + e_out) * spec.H + 2 * e_in * spec.kv_heads) * rows * spec.d + 4 * spec.H * rows
 
 
 def cpu_baseline_backward(w, budget_s: float):
@@ -137,6 +138,24 @@ def cpu_baseline(w, budget_s: float):
     s = w.spec
     q, k, v = w.exact()
     kl = w.key_len_or_none()
+    if s.packed:
+        done, flops = 0, 0.0
+        t0 = time.perf_counter()
+        for b, n in enumerate(w.lengths):
+            for h in range(s.H):
+                oracle.attention_varlen_rows(q, k, v, w.cu_seqlens, s.scale, s.causal, b, h,
+                                             range(int(n)))
+                done += 1
+                flops += s.flops([n]) / s.H
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"{done} of {s.B * s.H} (sequence, head) pairs of the same packed "
+                          f"batch, every row, float64, {dt:.2f} s wall"}
     if s.is_decode:
         done = 0
         t0 = time.perf_counter()
@@ -223,7 +242,8 @@ def main(argv=None):
     q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
     kl = None if w.key_len is None else torch.from_numpy(w.key_len).to(dev)
     o = torch.empty(q.shape, dtype=fa.out_dtype(q.dtype), device=dev)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    cu = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens).to(dev)
     stream = torch.cuda.current_stream()
     ws = None
     if spec.is_decode:
@@ -231,7 +251,7 @@ def main(argv=None):
         ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
     if args.backward:
-        if spec.is_decode or spec.dtype not in ("bf16", "fp16"):
+        if spec.is_decode or spec.packed or spec.dtype not in ("bf16", "fp16"):
             print(json.dumps({"error": "the backward covers 16-bit forward workloads"}))
             return 2
         o_f, lse_f = fa.fwd(q, k, v, scale=spec.scale, causal=spec.causal, key_len=kl)
@@ -246,6 +266,8 @@ def main(argv=None):
         if args.backward:
             fa.fa_bwd(q, k, v, o_f, dout, lse_f, *grads, ws, spec.scale, spec.causal, kl,
                       stream=stream)
+        elif spec.packed:
+            fa.fa_fwd_varlen(q, k, v, o, lse, cu, spec.N, spec.scale, spec.causal, stream=stream)
         elif spec.window_left >= 0:
             fa.fa_fwd_window(q, k, v, o, lse, spec.scale, spec.causal, (spec.window_left, -1), kl,
                              *w.descale, stream=stream)
@@ -302,12 +324,12 @@ def main(argv=None):
     ms_per_step = total_ms / args.steps
     avg_launch_ms = ms_per_step  # one step is one launch (decode and backward: their kernels)
 
-    flop = spec.flops() * (2.5 if args.backward else 1.0)
+    flop = w.flops() * (2.5 if args.backward else 1.0)
     value = flop / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[spec.dtype]
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     traffic = measured_traffic(spec.name) if default_n and not args.backward else None
-    exps = spec.exps()
+    exps = w.exps()
     if spec.is_decode:
         # HBM-bound: the roofline is bytes moved, the two kernels of a step
         # (split pass and merge) timed together
@@ -338,6 +360,9 @@ def main(argv=None):
             "causal": spec.causal, "scale": spec.scale,
             "H_kv": spec.kv_heads, "Nq": spec.q_len, "window_left": spec.window_left,
             "key_len": None if w.key_len is None else "per-batch padding",
+            "packed": None if cu is None else {
+                "sequences": spec.B, "rows": int(w.q.shape[1]),
+                "lengths": "U{%d..%d}" % spec.key_len_range, "max_seqlen": spec.N},
             "outlier_keys_frac": spec.outlier_frac, "seed": spec.seed,
             "spread_sample_steps": len(per),
             "launch_ms_p10": round(per[len(per) // 10], 5),
@@ -352,7 +377,7 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "algorithmic_bytes": algorithmic_bytes(spec),
+            "algorithmic_bytes": algorithmic_bytes(spec, None if cu is None else w.q.shape[1]),
             "kernel_sources_sha256_16": kernel_sha(),
             # Secondary bound: one exp2 per unmasked score on the transcendental
             # unit (256 CUs x 4 SIMDs x 8 lanes per cycle x 2.4 GHz).

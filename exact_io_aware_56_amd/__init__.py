@@ -1,7 +1,7 @@
 """Exact IO-aware attention forward for AMD Instinct MI355X (gfx950).
 
 Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_gqa`` /
-``fa_fwd_window`` / ``fa_fwd_decode`` / ``fa_bwd`` marshal torch tensors' device pointers and the current stream
+``fa_fwd_window`` / ``fa_fwd_varlen`` / ``fa_fwd_decode`` / ``fa_bwd`` marshal torch tensors' device pointers and the current stream
 into the C entry points of the same names; ``fwd`` (and its positional twin ``forward``) additionally
 allocates O and LSE. Nothing here computes any part of the attention.
 """
@@ -108,6 +108,46 @@ def fa_fwd_window(q, k, v, o, lse, scale: float, causal: bool = False, window=(-
                                        k.shape[1], N, d, scale, causal, window[0], window[1],
                                        _ptr(key_len), _DTYPE[q.dtype], q_descale, k_descale,
                                        v_descale, _stream(stream)))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float,
+                  causal: bool = False, stream=None) -> None:
+    """Enqueue fa_fwd_varlen: a packed batch, q [H, total, d], k, v [H_kv, total, d],
+    o like q, lse float32 [H, total], cu_seqlens device int32 [B + 1]."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse),
+                    ("cu_seqlens", cu_seqlens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [H, total, d] and k, v one [H_kv, total, d] shape")
+    H, total, d = q.shape
+    if k.shape[1:] != (total, d) or H % k.shape[0] != 0:
+        raise ValueError("k, v must be [H_kv, total, d] with H_kv dividing q's H")
+    if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if o.shape != q.shape or o.dtype != out_dtype(q.dtype):
+        raise ValueError("o must be [H, total, d] of the output dtype")
+    if lse.shape != (H, total) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [H, total]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2:
+        raise ValueError("cu_seqlens must be int32 [B + 1] with B >= 1")
+    _lib._check(_lib.fa_fwd_varlen_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _ptr(cu_seqlens), cu_seqlens.shape[0] - 1, H, k.shape[0],
+                                       total, max_seqlen, d, scale, causal, _DTYPE[q.dtype],
+                                       _stream(stream)))
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float, causal: bool = False,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(O, LSE) of a packed batch of sequences (see fa_fwd_varlen). O and LSE are
+    allocated here; rows outside every sequence are left as allocated (zero)."""
+    H, total, d = q.shape
+    o = torch.zeros((H, total, d), dtype=out_dtype(q.dtype), device=q.device)
+    lse = torch.zeros((H, total), dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, stream=stream)
+    return o, lse
 
 
 def forward(q, k, v, scale: float, causal: bool = False, key_len=None,

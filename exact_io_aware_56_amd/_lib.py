@@ -16,7 +16,7 @@ FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_decode", "fa_decode_workspace_bytes",
-            "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_status_str",
+            "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_fwd_varlen", "fa_status_str",
             "fa_abi_version", "fa_last_error")
 
 _lib = None
@@ -54,6 +54,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, f, f, f, vp]
     lib.fa_fwd_window.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_varlen.restype = i
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -121,3 +123,10 @@ def fa_fwd_window_raw(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, wl, wr, 
     return load().fa_fwd_window(q, k, v, o, lse, B, H, H_kv, N, d, float(scale), int(causal),
                                 int(wl), int(wr), key_len, int(dtype), float(qd), float(kd),
                                 float(vd), stream)
+
+
+def fa_fwd_varlen_raw(q, k, v, o, lse, cu_seqlens, B, H, H_kv, total, max_seqlen, d, scale,
+                      causal, dtype, stream) -> int:
+    return load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, int(B), int(H), int(H_kv),
+                                int(total), int(max_seqlen), int(d), float(scale), int(causal),
+                                int(dtype), stream)

@@ -77,8 +77,66 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   p.o_scale = vd;
   p.win_left = win_left < 0 ? -1 : win_left;
   p.win_right = win_right < 0 ? -1 : win_right;
+  p.cu_seqlens = nullptr;
+  p.total = 0;
 
   const hipError_t e = fa::launch_forward(kind, d, causal != 0, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+int varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           const int32_t* cu_seqlens, int B, int H, int H_kv, int total, int max_seqlen, int d,
+           float scale, int causal, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !O || !LSE || !cu_seqlens)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer or cu_seqlens is NULL");
+  if (B < 1 || H < 1 || total < 1 || max_seqlen < 1 || d < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H, total, max_seqlen and d must be >= 1");
+  if (H_kv < 1 || H % H_kv != 0) return fail(FA_ERR_INVALID_ARG, "H_kv must be >= 1 and divide H");
+  if (dtype < FA_DTYPE_FP32 || dtype > FA_DTYPE_FP8_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "dtype is not a fa_dtype value");
+  if (!positive_finite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(FA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
+  if (!aligned(LSE, 4) || !aligned(cu_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARG, "LSE and cu_seqlens must be 4-byte aligned");
+  if ((__int128)H * total * d * 4 > (__int128)INT64_MAX)
+    return fail(FA_ERR_INVALID_ARG, "H*total*d overflows");
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16)
+    return fail(FA_ERR_UNSUPPORTED, "packed batches take bfloat16 or float16 inputs");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  // No sequence is longer than the packed rows themselves.
+  const int n_max = max_seqlen < total ? max_seqlen : total;
+  if ((long long)n_max * d * 2 >= (1LL << 30))
+    return fail(FA_ERR_UNSUPPORTED, "one sequence's rows x d must be under 1 GiB");
+  const int rows = fa::varlen_rows_per_block(n_max, causal != 0);
+  fa::Params p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.key_len = nullptr;
+  p.B = B;
+  p.H = H;
+  p.kv_group = H / H_kv;
+  p.N = n_max;
+  p.n_qt = (n_max + rows - 1) / rows;
+  if ((long long)B * H * p.n_qt > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARG, "B*H*ceil(max_seqlen/rows) exceeds the grid limit");
+  p.scale_eff = scale;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.o_scale = 1.0f;
+  p.win_left = p.win_right = -1;
+  p.cu_seqlens = cu_seqlens;
+  p.total = total;
+  const hipError_t e =
+      fa::launch_forward_varlen(static_cast<fa::Kind>(dtype), d, causal != 0, p,
+                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     snprintf(g_last_error, sizeof g_last_error, "kernel launch failed: %s", hipGetErrorString(e));
     return FA_ERR_HIP;
@@ -296,6 +354,13 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
                   float k_descale, float v_descale, void* stream) {
   return forward(Q, K, V, O, LSE, B, H, H_kv, N, d, scale, causal, key_len, dtype, q_descale,
                  k_descale, v_descale, stream, window_left, window_right);
+}
+
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  const int32_t* cu_seqlens, int B, int H, int H_kv, int total, int max_seqlen,
+                  int d, float scale, int causal, int dtype, void* stream) {
+  return varlen(Q, K, V, O, LSE, cu_seqlens, B, H, H_kv, total, max_seqlen, d, scale, causal,
+                dtype, stream);
 }
 
 const char* fa_status_str(int status) {

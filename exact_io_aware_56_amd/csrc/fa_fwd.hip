@@ -249,6 +249,45 @@ __device__ __forceinline__ RowRange row_range(const Params& p, int wave, int l32
   return row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
 }
 
+// Packed batch: workgroup -> (sequence * H + head, unit), heads fastest.
+// Workgroups go to the XCDs round-robin by id, so consecutive ids (the heads
+// of one unit of one sequence) spread every sequence evenly over the XCDs,
+// whatever the mix of lengths; contiguous runs of whole heads per XCD would
+// leave the XCDs that own the longest sequences with most of the work.
+__device__ __forceinline__ void varlen_item(int H, int units, int& bh, int& u) {
+  const int bid = blockIdx.x;
+  const int h = bid % H, r = bid / H;
+  u = r % units;
+  bh = (r / units) * H + h;
+}
+
+// Packed batch: narrows p to the sequence and head of work item bh = b * H + h,
+// so that the kernel then runs as on one head of one batch entry: the Q, K, V,
+// O and LSE pointers move to the sequence's first row of the head's block and
+// N becomes the sequence's length. Bounds are clamped to [0, total] (an end
+// before its start gives an empty sequence) and the length is cut to the grid's
+// p.N. Returns false, the same in every lane, when query row q0 lies past the
+// sequence's end.
+template <class TIn, class TOut, int D>
+__device__ __forceinline__ bool enter_segment(Params& p, int bh, int q0) {
+  const int b = bh / p.H, h = bh - b * p.H, T = p.total;
+  int s0 = min(max(p.cu_seqlens[b], 0), T);
+  const int s1 = min(max(p.cu_seqlens[b + 1], s0), T);
+  const int n = __builtin_amdgcn_readfirstlane(min(s1 - s0, p.N));
+  s0 = __builtin_amdgcn_readfirstlane(s0);
+  if (q0 >= n) return false;
+  const size_t qrow = (size_t)h * T + s0, kvrow = (size_t)(h / p.kv_group) * T + s0;
+  p.q = (const TIn*)p.q + qrow * D;
+  p.k = (const TIn*)p.k + kvrow * D;
+  p.v = (const TIn*)p.v + kvrow * D;
+  p.o = (TOut*)p.o + qrow * D;
+  p.lse += qrow;
+  p.N = n;
+  p.key_len = nullptr;
+  p.B = p.H = p.kv_group = 1;
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit element policies
 // ---------------------------------------------------------------------------
@@ -786,7 +825,7 @@ __device__ __forceinline__ void wait_vmem_keep() {
 // operand reads and their latency in front of each MFMA, not the arithmetic,
 // bound the register-staged kernel above; this one trims them.
 // ---------------------------------------------------------------------------
-template <class E, int D, int BC, int NW, int NBUF, bool CAUSAL, bool WIN = false>
+template <class E, int D, int BC, int NW, int NBUF, bool CAUSAL, bool WIN = false, bool VL = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   using T = typename E::T;
   using v8 = typename E::v8;
@@ -819,7 +858,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
+  RowRange rr;
+  if constexpr (VL) {
+    // Packed batch: the item's sequence becomes a one-head problem.
+    int bh, r;
+    varlen_item(p.H, p.n_qt, bh, r);
+    const int qt = CAUSAL ? p.n_qt - 1 - r : r;  // longest query tiles first
+    if (!enter_segment<T, T, D>(p, bh, qt * BR)) return;
+    rr = row_range_at<BR, BC, CAUSAL>(p, 0, qt, wave, l32);
+  } else {
+    rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
+  }
   const int N = p.N;
   // Sliding window: the workgroup streams tiles [t0, nt); this wave computes
   // [wt0, wnt) of them, of which [whead, wfull) need no mask.
@@ -1009,7 +1058,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // range, see row_range), and it is the wave's last tile.
 // ---------------------------------------------------------------------------
 
-template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8>
+template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8, bool VL = false>
 __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   using T = typename E::T;  // P, V in LDS and O (bfloat16 for fp8 inputs)
   using v8 = typename E::v8;
@@ -1017,6 +1066,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   using QT = std::conditional_t<F8, i32x8, v8>;  // one Q or K operand of the S product
   static_assert(G == 1 || G == 2, "one or two 32-row groups per wave");
   static_assert(!F8 || (G == 1 && NB == 2), "fp8 inputs: one row group, two buffers");
+  static_assert(!(F8 && VL), "packed batches take 16-bit inputs");
   constexpr int WR = 32 * G;   // query rows per wave
   constexpr int BR = NW * WR;  // query rows per workgroup
   constexpr int BC = 64;       // keys per LDS tile
@@ -1059,6 +1109,34 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
+
+  // The workgroup's work unit u of head bh. Causal work is folded: a
+  // workgroup takes query tile n_qt-1-u and then tile u of one head, so every
+  // workgroup streams n_qt+1 key-tile runs and the launch needs no
+  // longest-first order to stay balanced; the workgroups are then issued head
+  // by head, and those that run together on an XCD stream the same heads' K/V
+  // through its L2. The middle tile of an odd n_qt is one workgroup's only
+  // tile.
+  const int units = CAUSAL ? (p.n_qt + 1) / 2 : p.n_qt;
+  int bh, u;
+  if constexpr (VL) {
+    varlen_item(p.H, units, bh, u);
+  } else {
+    const int bid = blockIdx.x, total = gridDim.x;
+    int logical = bid;
+    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+    bh = logical / units;
+    u = logical - bh * units;
+  }
+  int n_qt = p.n_qt;
+  if constexpr (VL) {
+    // Packed batch: the item's sequence becomes a one-head problem whose
+    // query tiles are folded the same way; units past them have no work.
+    if (!enter_segment<T, T, D>(p, bh, u * BR)) return;
+    bh = 0;
+    n_qt = (p.N + BR - 1) / BR;
+    if (CAUSAL && u >= (n_qt + 1) / 2) return;
+  }
   const int N = p.N;
 
   // Q^T operand: lane holds its query row's head-dim elements
@@ -1413,21 +1491,10 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   if constexpr (!PF) __syncthreads();
   };
 
-  // Causal work is folded: a workgroup takes query tile n_qt-1-u and then
-  // tile u of one head, so every workgroup streams n_qt+1 key-tile runs and
-  // the launch needs no longest-first order to stay balanced; the workgroups
-  // are then issued head by head, and those that run together on an XCD
-  // stream the same heads' K/V through its L2. The middle tile of an odd
-  // n_qt is one workgroup's only tile.
-  const int units = CAUSAL ? (p.n_qt + 1) / 2 : p.n_qt;
-  const int bid = blockIdx.x, total = gridDim.x;
-  int logical = bid;
-  if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
-  const int bh = logical / units, u = logical - bh * units;
-  const int items = CAUSAL && u != p.n_qt - 1 - u ? 2 : 1;
+  const int items = CAUSAL && u != n_qt - 1 - u ? 2 : 1;
 #pragma nounroll
   for (int it = 0; it < items; ++it)
-    process(bh, CAUSAL && it == 0 ? p.n_qt - 1 - u : u, it > 0, it + 1 < items, bh, u);
+    process(bh, CAUSAL && it == 0 ? n_qt - 1 - u : u, it > 0, it + 1 < items, bh, u);
 }
 
 // ---------------------------------------------------------------------------
@@ -2543,6 +2610,17 @@ hipError_t launch_16bit(const Params& p, hipStream_t s) {
 #endif
 }
 
+// Packed batches take the kernel a single sequence of the longest length
+// would take (p.N is that length).
+template <class E, int D, bool C>
+hipError_t launch_16bit_varlen(const Params& p, hipStream_t s) {
+  if (use_pipe(p.N, C))
+    return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false, true>,
+                  p, FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
+  return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C, false, true>, p,
+                FA_DMA_WAVES * 64, s);
+}
+
 template <int D, bool C>
 hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
   constexpr int T = kWaves * 64;
@@ -2590,6 +2668,23 @@ hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStr
   }
   if (d == 64) return causal ? launch_d<64, true>(kind, p, stream) : launch_d<64, false>(kind, p, stream);
   if (d == 128) return causal ? launch_d<128, true>(kind, p, stream) : launch_d<128, false>(kind, p, stream);
+  return hipErrorInvalidValue;
+}
+
+int varlen_rows_per_block(int max_seqlen, bool causal) {
+  return use_pipe(max_seqlen, causal) ? FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS : FA_DMA_WAVES * 32;
+}
+
+hipError_t launch_forward_varlen(Kind kind, int d, bool causal, const Params& p,
+                                 hipStream_t stream) {
+  if (p.cu_seqlens == nullptr) return hipErrorInvalidValue;
+  if (kind == Kind::BF16) {
+    if (d == 64) return causal ? launch_16bit_varlen<Bf16, 64, true>(p, stream) : launch_16bit_varlen<Bf16, 64, false>(p, stream);
+    if (d == 128) return causal ? launch_16bit_varlen<Bf16, 128, true>(p, stream) : launch_16bit_varlen<Bf16, 128, false>(p, stream);
+  } else if (kind == Kind::F16) {
+    if (d == 64) return causal ? launch_16bit_varlen<F16, 64, true>(p, stream) : launch_16bit_varlen<F16, 64, false>(p, stream);
+    if (d == 128) return causal ? launch_16bit_varlen<F16, 128, true>(p, stream) : launch_16bit_varlen<F16, 128, false>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -23,6 +23,11 @@ struct Params {
   float o_scale;    // v_descale
   int win_left;     // sliding window: keys j >= i - win_left (negative: unbounded)
   int win_right;    // and j <= i + win_right (negative: unbounded)
+  // Packed batch (NULL otherwise): B sequences concatenated along the rows of
+  // every head's [total, D] block, sequence b at rows [cu_seqlens[b],
+  // cu_seqlens[b+1]); N is then the longest length the grid covers.
+  const int32_t* cu_seqlens;
+  int total;
 };
 
 // Decode (few queries against a key/value cache), split over keys.
@@ -74,6 +79,14 @@ int rows_per_block(Kind kind, int d, int N, bool causal, bool window = false);
 // Enqueue the forward on `stream`. Arguments are already validated and
 // p.n_qt filled in. Returns the launch's hipError_t.
 hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream);
+
+// Rows of Q per workgroup of the packed-batch forward (16-bit kinds, d 64 / 128)
+// whose longest sequence has max_seqlen rows.
+int varlen_rows_per_block(int max_seqlen, bool causal);
+
+// Enqueue the packed-batch forward (p.cu_seqlens set, p.n_qt over p.N).
+hipError_t launch_forward_varlen(Kind kind, int d, bool causal, const Params& p,
+                                 hipStream_t stream);
 
 // Key chunks S (and 32-key tiles per chunk) for `units_base` = B*H_kv*n_rb
 // (K/V head, row block) pairs over Nk keys. Deterministic in its arguments:

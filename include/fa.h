@@ -46,7 +46,8 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd; 5: fa_fwd_window */
+#define FA_ABI_VERSION 6  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd; 5: fa_fwd_window;
+                             6: fa_fwd_varlen */
 
 typedef enum {
   FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
@@ -145,6 +146,44 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
                   int B, int H, int H_kv, int N, int d, float scale, int causal,
                   int window_left, int window_right, const int32_t* key_len, int dtype,
                   float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
+ * fa_fwd_varlen -- a packed batch of B sequences of unequal length (packed
+ * variable-length batches are among the richer masks named through the
+ * FlashMask title in the bibliography of FlashAttention (ES)). The sequences
+ * are concatenated along the row axis of every head, and each one is attended
+ * on its own, exactly as fa_fwd_gqa would attend it as a batch entry of its own
+ * length with every key valid.
+ *
+ *   Q          [in]  device, [H,total,d] of `dtype`: row r of head h is
+ *                    Q + (h*total + r)*d
+ *   K, V       [in]  device, [H_kv,total,d] of `dtype`
+ *   O          [out] device, [H,total,d] of `dtype`
+ *   LSE        [out] device, float [H,total], natural log
+ *   cu_seqlens [in]  device, int32 [B+1]: sequence b holds rows
+ *                    [cu_seqlens[b], cu_seqlens[b+1]); meant to be
+ *                    non-decreasing from 0 to total
+ *   B          sequences, >= 1
+ *   H, H_kv    query and K/V heads, grouped as in fa_fwd_gqa
+ *   total      packed rows per head, >= 1
+ *   max_seqlen the longest sequence, >= 1: the grid covers this many rows
+ *              per sequence
+ *   d, scale, causal, dtype, stream as fa_fwd_gqa (causal: row i of a
+ *              sequence sees that sequence's keys 0..i)
+ *
+ * Device-side bounds: each cu_seqlens value is clamped to [0, total], an end
+ * below its start is taken as the start (an empty sequence), and a sequence
+ * longer than max_seqlen is cut to its first max_seqlen rows. Rows of O and LSE
+ * outside every (cut) sequence are not written. Overlapping sequences (a
+ * decreasing cu_seqlens) give unspecified values in the overlap but stay
+ * within the buffers. bfloat16 / float16 inputs with d 64 or 128 (others:
+ * FA_ERR_UNSUPPORTED); a NULL cu_seqlens, B, H, total, max_seqlen < 1 or an
+ * H_kv not dividing H return FA_ERR_INVALID_ARG. The library allocates
+ * nothing.
+ */
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  const int32_t* cu_seqlens, int B, int H, int H_kv, int total,
+                  int max_seqlen, int d, float scale, int causal, int dtype, void* stream);
 
 /*
  * fa_fwd_decode -- the newest Nq queries of each batch entry against its

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 5
+    assert lib.fa_abi_version() == 6
     assert _lib.status_name(0) == "FA_OK"
     assert _lib.status_name(-1) == "FA_ERR_INVALID_ARG"
     assert _lib.status_name(-2) == "FA_ERR_UNSUPPORTED"
@@ -150,6 +150,28 @@ def window_call(**kw):
 ])
 def test_window_entry_point_rejects_bad_arguments(kw, status):
     assert window_call(**kw) == status
+    assert _lib.load().fa_last_error().decode() != ""
+
+
+def varlen_call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cu=P, B=3, H=4, H_kv=2, total=100, max_seqlen=50, d=64,
+             scale=0.125, causal=1, dtype=2, stream=None)
+    a.update(kw)
+    return _lib.fa_fwd_varlen_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"],
+                                  a["H"], a["H_kv"], a["total"], a["max_seqlen"], a["d"],
+                                  a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), -1), (dict(q=None), -1), (dict(lse=None), -1), (dict(B=0), -1),
+    (dict(H=0), -1), (dict(total=0), -1), (dict(max_seqlen=0), -1), (dict(H_kv=3), -1),
+    (dict(dtype=7), -1), (dict(scale=math.nan), -1), (dict(k=P + 8), -1), (dict(cu=P + 2), -1),
+    (dict(dtype=0), -2), (dict(dtype=3), -2), (dict(d=256), -2), (dict(d=96), -2),
+    (dict(total=1 << 23, max_seqlen=1 << 23), -2),
+    (dict(B=1 << 30, H=8, max_seqlen=1000, total=100000), -1),
+])
+def test_varlen_entry_point_rejects_bad_arguments(kw, status):
+    assert varlen_call(**kw) == status
     assert _lib.load().fa_last_error().decode() != ""
 
 
