@@ -102,6 +102,12 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_PIPE_PREFETCH
 #define FA_PIPE_PREFETCH 0  // pipelined kernel: next causal item's Q and first tiles under the epilogue
 #endif
+#ifndef FA_PIPE_FENCE
+// pipelined 16-bit kernel: S and P V products of a half-step as one operand
+// stream whose LDS reads are held FA_PIPE_LOOKAHEAD products ahead by
+// scheduling fences (0: the compiler places the reads)
+#define FA_PIPE_FENCE 1
+#endif
 #ifndef FA_PIPE_NBUF
 #define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
 #endif
@@ -1058,6 +1064,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // range, see row_range), and it is the wave's last tile.
 // ---------------------------------------------------------------------------
 
+// Bit cast between operand types of one size; a zero value otherwise (for
+// code paths that a kernel variant compiles but never takes).
+template <class To, class From>
+__device__ __forceinline__ To same_size_cast(const From& x) {
+  if constexpr (sizeof(To) == sizeof(From)) return __builtin_bit_cast(To, x);
+  else return To{};
+}
+
 template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8, bool VL = false>
 __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   using T = typename E::T;  // P, V in LDS and O (bfloat16 for fp8 inputs)
@@ -1375,13 +1389,53 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // One iteration: tile t's V (vb) and tile t+1's K (kb). On entry sb holds
   // S of half 2t+1 and pfa P of half 2t; on exit sb holds S of half 2t+3 and
   // pfa P of half 2t+2.
+  // The S product of half h of the K tile at kb (when hn) and O += V^T P^T of
+  // half h of the V tile at vb as one stream of products: each operand read
+  // is issued LA products before the product that takes it, and fences that
+  // only vector ALU, scalar and global-memory instructions may cross keep the
+  // scheduler from sinking the reads back to their products (which would
+  // leave every product waiting out a whole LDS latency). The softmax
+  // arithmetic that follows in program order still moves up among them.
+  constexpr int kFence = 0x2 | 0x4 | 0x10 | 0x400;  // VALU, SALU, VMEM, transcendental
+  auto mma_half = [&](const unsigned char* kb, int h, f32x16 (&s)[G], const unsigned char* vb,
+                      const v8 (&pf)[G][2], auto hn) __attribute__((always_inline)) {
+    constexpr int NS = decltype(hn)::value ? KS : 0;
+    constexpr int NT = NS + NPV;
+    if constexpr (NS > 0)
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g] = f32x16{};
+    v8 ring[LA + 1];
+#pragma unroll
+    for (int t = 0; t < NT + LA; ++t) {
+      if (t < NT) {
+        if (t < NS) ring[t % (LA + 1)] = same_size_cast<v8>(kfrag(kb, h, t));
+        else ring[t % (LA + 1)] = vfrag(vb, h, t - NS);
+        __builtin_amdgcn_sched_barrier(kFence);
+      }
+      const int u = t - LA;
+      if (u >= 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (u < NS) s[g] = E::mma(ring[u % (LA + 1)], same_size_cast<v8>(qf[g][u]), s[g]);
+          else o[g][(u - NS) % DB] = E::mma(ring[u % (LA + 1)], pf[g][(u - NS) / DB], o[g][(u - NS) % DB]);
+        }
+        __builtin_amdgcn_sched_barrier(kFence);
+      }
+    }
+  };
   auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next,
                        auto mask_a, auto mask_b) __attribute__((always_inline)) {
-    if constexpr (decltype(has_next)::value) scores(kb, 0, sa);
-    pv(vb, 0, pfa);
-    probs(sb, pfb, BC * t + 32, mask_a);
-    if constexpr (decltype(has_next)::value) scores(kb, 1, sb);
-    pv(vb, 1, pfb);
+    if constexpr (FA_PIPE_FENCE && !F8) {
+      mma_half(kb, 0, sa, vb, pfa, has_next);
+      probs(sb, pfb, BC * t + 32, mask_a);
+      mma_half(kb, 1, sb, vb, pfb, has_next);
+    } else {
+      if constexpr (decltype(has_next)::value) scores(kb, 0, sa);
+      pv(vb, 0, pfa);
+      probs(sb, pfb, BC * t + 32, mask_a);
+      if constexpr (decltype(has_next)::value) scores(kb, 1, sb);
+      pv(vb, 1, pfb);
+    }
     if constexpr (decltype(has_next)::value) probs(sa, pfa, BC * (t + 1), mask_b);
   };
   // K tile j lives in buffer j % NB, V tile j in buffer j % NB. Iteration t
