@@ -105,8 +105,12 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_PIPE_FENCE
 // pipelined 16-bit kernel: S and P V products of a half-step as one operand
 // stream whose LDS reads are held FA_PIPE_LOOKAHEAD products ahead by
-// scheduling fences (0: the compiler places the reads)
+// scheduling fences (0: the compiler places the reads; 2: the softmax of the
+// previous half is also placed by hand, one score per product)
 #define FA_PIPE_FENCE 1
+#endif
+#ifndef FA_PIPE_ORDER
+#define FA_PIPE_ORDER 0  // fenced stream: 0 every S product first, 1 S and P V alternating
 #endif
 #ifndef FA_PIPE_NBUF
 #define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
@@ -311,6 +315,11 @@ struct Bf16 {
     return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)lds));
   }
   static __device__ __forceinline__ T cvt(float x) { return (T)x; }
+  // acc + a + b (already rounded values), fp32 accumulation
+  static __device__ __forceinline__ float sum2(T a, T b, float acc) {
+    const bf16x2 one = {(T)1.0f, (T)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a, b}, one, acc, false);
+  }
   // acc + sum of the 8 (already rounded) values, fp32 accumulation
   static __device__ __forceinline__ float sum8(v8 x, float acc) {
     const bf16x2 one = {(T)1.0f, (T)1.0f};
@@ -333,6 +342,10 @@ struct F16 {
     return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)lds));
   }
   static __device__ __forceinline__ T cvt(float x) { return (T)x; }
+  static __device__ __forceinline__ float sum2(T a, T b, float acc) {
+    const f16x2 one = {(T)1.0f, (T)1.0f};
+    return __builtin_amdgcn_fdot2(f16x2{a, b}, one, acc, false);
+  }
   static __device__ __forceinline__ float sum8(v8 x, float acc) {
     const f16x2 one = {(T)1.0f, (T)1.0f};
 #pragma unroll
@@ -1404,13 +1417,72 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
     if constexpr (NS > 0)
 #pragma unroll
       for (int g = 0; g < G; ++g) s[g] = f32x16{};
+    // stream position t -> S step (is_s) or P V step, and its index
+    constexpr bool ALT = FA_PIPE_ORDER == 1 && NS == NPV;
+    auto is_s = [](int t) { return ALT ? t % 2 == 0 : t < NS; };
+    auto idx = [](int t) { return ALT ? t / 2 : t < NS ? t : t - NS; };
     v8 ring[LA + 1];
+#pragma unroll
+    for (int t = 0; t < NT + LA; ++t) {
+      if (t < NT) {
+        if (is_s(t)) ring[t % (LA + 1)] = same_size_cast<v8>(kfrag(kb, h, idx(t)));
+        else ring[t % (LA + 1)] = vfrag(vb, h, idx(t));
+        __builtin_amdgcn_sched_barrier(kFence);
+      }
+      const int u = t - LA;
+      if (u >= 0) {
+        const int i = idx(u);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (is_s(u)) s[g] = E::mma(ring[u % (LA + 1)], same_size_cast<v8>(qf[g][i]), s[g]);
+          else o[g][i % DB] = E::mma(ring[u % (LA + 1)], pf[g][i / DB], o[g][i % DB]);
+        }
+        __builtin_amdgcn_sched_barrier(kFence);
+      }
+    }
+  };
+  // mma_half with the softmax of another half (raw scores s_in -> P pf_out)
+  // spread evenly under its products in program order, nothing allowed to
+  // move across: each product slot takes its share of the scores' FMA and
+  // exponential, and the conversion and row sum of the pair finished one
+  // slot earlier. Ends with the bound check of probs.
+  auto unit = [&](const unsigned char* kb, int h, f32x16 (&s)[G], const unsigned char* vb,
+                  const v8 (&pf)[G][2], f32x16 (&s_in)[G], v8 (&pf_out)[G][2], int k0, auto hn,
+                  auto masked, auto dp) __attribute__((always_inline)) {
+    constexpr bool DP = decltype(dp)::value;
+    constexpr int NS = decltype(hn)::value ? KS : 0;
+    constexpr int NT = NS + NPV;
+    constexpr int SPS = 16 / NT;  // scores per product slot
+    static_assert(16 % NT == 0, "whole scores per slot");
+    constexpr int kHard = 0x4 | 0x10;  // only scalar and global-memory instructions cross
+    float rs[G], e[G][16];
+    if constexpr (DP) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if constexpr (decltype(masked)::value)
+          apply_mask<1, CAUSAL>(*reinterpret_cast<f32x16(*)[1]>(&s_in[g]), k0, rr.kl, rr.qrow + 32 * g, hi);
+        rs[g] = 0.0f;
+      }
+    }
+    auto pair_done = [&](int i) __attribute__((always_inline)) {  // scores i, i+1 -> P, row sum
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        pf_out[g][i / 8][i % 8] = E::cvt(e[g][i]);
+        pf_out[g][i / 8][i % 8 + 1] = E::cvt(e[g][i + 1]);
+        rs[g] = E::sum2(pf_out[g][i / 8][i % 8], pf_out[g][i / 8][i % 8 + 1], rs[g]);
+      }
+    };
+    if constexpr (NS > 0)
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g] = f32x16{};
+    v8 ring[LA + 1];
+    __builtin_amdgcn_sched_barrier(kHard);
 #pragma unroll
     for (int t = 0; t < NT + LA; ++t) {
       if (t < NT) {
         if (t < NS) ring[t % (LA + 1)] = same_size_cast<v8>(kfrag(kb, h, t));
         else ring[t % (LA + 1)] = vfrag(vb, h, t - NS);
-        __builtin_amdgcn_sched_barrier(kFence);
+        __builtin_amdgcn_sched_barrier(kHard);
       }
       const int u = t - LA;
       if (u >= 0) {
@@ -1419,12 +1491,41 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
           if (u < NS) s[g] = E::mma(ring[u % (LA + 1)], same_size_cast<v8>(qf[g][u]), s[g]);
           else o[g][(u - NS) % DB] = E::mma(ring[u % (LA + 1)], pf[g][(u - NS) / DB], o[g][(u - NS) % DB]);
         }
-        __builtin_amdgcn_sched_barrier(kFence);
+        __builtin_amdgcn_sched_barrier(kHard);
+        if constexpr (DP) {
+#pragma unroll
+          for (int k = 0; k < SPS; ++k) {
+            const int i = u * SPS + k;
+#pragma unroll
+            for (int g = 0; g < G; ++g) e[g][i] = fast_exp2(fmaf(s_in[g][i], c, base[g]));
+          }
+          // the pairs whose second exponential was issued a slot earlier
+#pragma unroll
+          for (int i = 0; i < 16; i += 2)
+            if (i + 1 >= (u - 1) * SPS && i + 1 < u * SPS) pair_done(i);
+          __builtin_amdgcn_sched_barrier(kHard);
+        }
       }
+    }
+    if constexpr (DP) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2)
+        if (i + 1 >= (NT - 1) * SPS) pair_done(i);
+      bool bad = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) bad |= !(rs[g] <= E::kPBound);
+      if (__builtin_amdgcn_ballot_w64(bad) != 0) fix_probs(s_in, pf_out, rs);
+#pragma unroll
+      for (int g = 0; g < G; ++g) l[g] += rs[g];
     }
   };
   auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next,
                        auto mask_a, auto mask_b) __attribute__((always_inline)) {
+    if constexpr (FA_PIPE_FENCE == 2 && !F8) {
+      unit(kb, 0, sa, vb, pfa, sb, pfb, BC * t + 32, has_next, mask_a, std::true_type{});
+      unit(kb, 1, sb, vb, pfb, sa, pfa, BC * (t + 1), has_next, mask_b, has_next);
+      return;
+    }
     if constexpr (FA_PIPE_FENCE && !F8) {
       mma_half(kb, 0, sa, vb, pfa, has_next);
       probs(sb, pfb, BC * t + 32, mask_a);
