@@ -109,6 +109,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 // previous half is also placed by hand, one score per product)
 #define FA_PIPE_FENCE 1
 #endif
+#ifndef FA_D256_FENCE
+#define FA_D256_FENCE 1  // head dim 256: operand reads held one product ahead by fences
+#endif
 #ifndef FA_PIPE_ORDER
 #define FA_PIPE_ORDER 0  // fenced stream: 0 every S product first, 1 S and P V alternating
 #endif
@@ -140,6 +143,13 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scheduling fence that only vector ALU, scalar, global-memory and
+// transcendental instructions may cross: LDS operand reads and matrix products
+// keep their program order, so a read issued ahead of the product before the
+// one that takes it stays there (the scheduler otherwise sinks each read onto
+// its product and every product waits out a whole LDS latency).
+__device__ __forceinline__ void operand_fence() { __builtin_amdgcn_sched_barrier(0x2 | 0x4 | 0x10 | 0x400); }
 
 // Returns x unchanged, but through an asm statement the optimizer cannot look
 // into or move. Used inside the rarely taken O-rescale branches: without it
@@ -741,15 +751,56 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_d256(Params p) {
     gload(j + 1);
     auto tile = [&](auto masked) __attribute__((always_inline)) {
       f32x16 sc[1] = {f32x16{}};
+      if constexpr (FA_D256_FENCE) {
+        // operand reads held one product ahead (operand_fence)
+        v8 ring[2];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const v8 a = *(const v8*)(ks[buf] + l32 * KST + 16 * st + 8 * hi);
-        sc[0] = E::mma(a, qf[st], sc[0]);
+        for (int t = 0; t <= KS; ++t) {
+          if (t < KS) {
+            ring[t & 1] = *(const v8*)(ks[buf] + l32 * KST + 16 * t + 8 * hi);
+            operand_fence();
+          }
+          if (t > 0) {
+            sc[0] = E::mma(ring[(t - 1) & 1], qf[t - 1], sc[0]);
+            operand_fence();
+          }
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const v8 a = *(const v8*)(ks[buf] + l32 * KST + 16 * st + 8 * hi);
+          sc[0] = E::mma(a, qf[st], sc[0]);
+        }
       }
       if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(sc, j * BC, rr.kl, rr.qrow, hi);
       v8 pf[2];
       online_softmax<E, 1, DB>(sc, p.c, thr, m, l, o, pf);
-      pv_product<E, 1, DB, VST>(vs[buf], lane, pf, o);
+      if constexpr (FA_D256_FENCE) {
+        // O^T += V^T P^T as pv_product computes it, reads one product ahead
+        const int row = 4 * hi + ((lane & 15) >> 2);
+        const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        auto vread = [&](int u) __attribute__((always_inline)) {
+          const T* b = vs[buf] + (16 * (u / DB) + row) * VST + 32 * (u % DB) + col;
+          const auto a0 = E::tr4(b);
+          const auto a1 = E::tr4(b + 8 * VST);
+          return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        v8 ring[2];
+#pragma unroll
+        for (int t = 0; t <= 2 * DB; ++t) {
+          if (t < 2 * DB) {
+            ring[t & 1] = vread(t);
+            operand_fence();
+          }
+          if (t > 0) {
+            const int u = t - 1;
+            o[u % DB] = E::mma(ring[u & 1], pf[u / DB], o[u % DB]);
+            operand_fence();
+          }
+        }
+      } else {
+        pv_product<E, 1, DB, VST>(vs[buf], lane, pf, o);
+      }
     };
     if (j < rr.wfull) tile(std::false_type{});
     else if (j < rr.wnt) tile(std::true_type{});
@@ -2085,6 +2136,15 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 #ifndef FA_BWD_KV_OCC
 #define FA_BWD_KV_OCC 2  // waves per SIMD the dK/dV pass is compiled for (1: 512 registers)
 #endif
+#ifndef FA_BWD_FENCE
+// backward passes: operand reads held ahead of their products by scheduling
+// fences, FA_BWD_FENCE_LA products ahead (0: the compiler places the reads,
+// FA_BWD_LOOKAHEAD ahead in program order)
+#define FA_BWD_FENCE 0
+#endif
+#ifndef FA_BWD_FENCE_LA
+#define FA_BWD_FENCE_LA 1
+#endif
 #ifndef FA_BWD_LOOKAHEAD
 #define FA_BWD_LOOKAHEAD 2  // backward passes: LDS operand reads issued this many MFMAs ahead
 #endif
@@ -2420,6 +2480,8 @@ struct SwzTile {
   __device__ __forceinline__ int row(int c) const { return roff + ((c ^ sw) << 4); }
 };
 
+constexpr int kBwdLA = FA_BWD_FENCE ? FA_BWD_FENCE_LA : FA_BWD_LOOKAHEAD;
+
 // acc^T[n][col] += sum_k Y[k][n] * M[k][col] over the 32 rows k of a swizzled
 // tile Y, M given as the packed 16-bit operand of a D-layout accumulator.
 template <class E, int D>
@@ -2427,7 +2489,7 @@ __device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzT
                                            const typename E::v8 (&m)[2], f32x16 (&acc)[D / 32]) {
   using v4 = typename E::v4;
   using v8 = typename E::v8;
-  constexpr int DB = D / 32, RB = D * 2, LA = FA_BWD_LOOKAHEAD;
+  constexpr int DB = D / 32, RB = D * 2, LA = kBwdLA;
   v8 ring[LA + 1];
 #pragma unroll
   for (int t = 0; t < 2 * DB + LA; ++t) {
@@ -2437,9 +2499,13 @@ __device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzT
       const v4 a1 = __builtin_bit_cast(
           v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
       ring[t % (LA + 1)] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      if constexpr (FA_BWD_FENCE) operand_fence();
     }
     const int u = t - LA;
-    if (u >= 0) acc[u % DB] = E::mma(ring[u % (LA + 1)], m[u / DB], acc[u % DB]);
+    if (u >= 0) {
+      acc[u % DB] = E::mma(ring[u % (LA + 1)], m[u / DB], acc[u % DB]);
+      if constexpr (FA_BWD_FENCE) operand_fence();
+    }
   }
 }
 
@@ -2448,13 +2514,19 @@ template <class E, int D>
 __device__ __forceinline__ void one_product(const unsigned char* x, const SwzTile<D>& sz, int hi,
                                             const typename E::v8 (&y)[D / 16], f32x16& s) {
   using v8 = typename E::v8;
-  constexpr int KS = D / 16, LA = FA_BWD_LOOKAHEAD;
+  constexpr int KS = D / 16, LA = kBwdLA;
   v8 ra[LA + 1];
 #pragma unroll
   for (int t = 0; t < KS + LA; ++t) {
-    if (t < KS) ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
+    if (t < KS) {
+      ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
+      if constexpr (FA_BWD_FENCE) operand_fence();
+    }
     const int u = t - LA;
-    if (u >= 0) s = E::mma(ra[u % (LA + 1)], y[u], s);
+    if (u >= 0) {
+      s = E::mma(ra[u % (LA + 1)], y[u], s);
+      if constexpr (FA_BWD_FENCE) operand_fence();
+    }
   }
 }
 
@@ -2468,18 +2540,20 @@ __device__ __forceinline__ void two_products(const unsigned char* x, const unsig
                                              const typename E::v8 (&w)[D / 16], f32x16& s,
                                              f32x16& dp) {
   using v8 = typename E::v8;
-  constexpr int KS = D / 16, LA = FA_BWD_LOOKAHEAD;
+  constexpr int KS = D / 16, LA = kBwdLA;
   v8 ra[LA + 1], rb[LA + 1];
 #pragma unroll
   for (int t = 0; t < KS + LA; ++t) {
     if (t < KS) {
       ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
       rb[t % (LA + 1)] = *(const v8*)(z + sz.row(2 * t + hi));
+      if constexpr (FA_BWD_FENCE) operand_fence();
     }
     const int u = t - LA;
     if (u >= 0) {
       s = E::mma(ra[u % (LA + 1)], y[u], s);
       dp = E::mma(rb[u % (LA + 1)], w[u], dp);
+      if constexpr (FA_BWD_FENCE) operand_fence();
     }
   }
 }
