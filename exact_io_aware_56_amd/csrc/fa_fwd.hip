@@ -109,6 +109,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 // previous half is also placed by hand, one score per product)
 #define FA_PIPE_FENCE 1
 #endif
+#ifndef FA_DMA_FENCE
+#define FA_DMA_FENCE 1  // direct-to-LDS kernel: operand reads held FA_LOOKAHEAD products ahead by fences
+#endif
 #ifndef FA_D256_FENCE
 #define FA_D256_FENCE 1  // head dim 256: operand reads held one product ahead by fences
 #endif
@@ -1020,14 +1023,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
     v8 ring[LA + 1];
 #pragma unroll
     for (int t = 0; t < NS + LA; ++t) {
-      if (t < NS) ring[t % (LA + 1)] = kfrag(kb, t);
+      if (t < NS) {
+        ring[t % (LA + 1)] = kfrag(kb, t);
+        if constexpr (FA_DMA_FENCE) operand_fence();
+      }
       const int u = t - LA;
-      if (u >= 0) s[u / KS] = E::mma(ring[u % (LA + 1)], qf[u % KS], s[u / KS]);
+      if (u >= 0) {
+        s[u / KS] = E::mma(ring[u % (LA + 1)], qf[u % KS], s[u / KS]);
+        if constexpr (FA_DMA_FENCE) operand_fence();
+      }
     }
     // first V operands, in flight during the softmax
     v8 vring[LA + 1];
 #pragma unroll
     for (int t = 0; t < LA; ++t) vring[t] = vfrag(vb, t);
+    if constexpr (FA_DMA_FENCE) operand_fence();
     if constexpr (decltype(masked)::value) {
       if constexpr (WIN)
         apply_mask_window<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi, p.win_left, p.win_right);
@@ -1039,9 +1049,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
     // O += P V, operand reads LA steps ahead
 #pragma unroll
     for (int t = LA; t < NPV + LA; ++t) {
-      if (t < NPV) vring[t % (LA + 1)] = vfrag(vb, t);
+      if (t < NPV) {
+        vring[t % (LA + 1)] = vfrag(vb, t);
+        if constexpr (FA_DMA_FENCE) operand_fence();
+      }
       const int u = t - LA;
       o[u % DB] = E::mma(vring[u % (LA + 1)], pf[u / DB], o[u % DB]);
+      if constexpr (FA_DMA_FENCE) operand_fence();
     }
   };
   // Iteration j uses buffer j % NBUF and copies tile j + NBUF - 1 into the
