@@ -112,6 +112,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_DMA_FENCE
 #define FA_DMA_FENCE 1  // direct-to-LDS kernel: operand reads held FA_LOOKAHEAD products ahead by fences
 #endif
+#ifndef FA_D256_PIPE
+#define FA_D256_PIPE 1  // head dim 256 on the pipelined kernel (column slices) where d = 128 takes it
+#endif
 #ifndef FA_D256_FENCE
 #define FA_D256_FENCE 1  // head dim 256: operand reads held one product ahead by fences
 #endif
@@ -516,10 +519,14 @@ __device__ __forceinline__ void epilogue(const Params& p, const RowRange& rr, in
 // each global store covers whole rows. Written straight from the accumulator
 // layout a row leaves a lane pair as 8-byte pieces, and lines that L2 evicts
 // half written cost extra memory writes.
-template <class OutT, int D, int DB>
+// D: columns this call writes (one row of the stage); DO: elements per row of
+// O in memory, the columns starting at col0 (a column slice when DO > D); LSE
+// is written only when lse is set.
+template <class OutT, int D, int DB, int DO = D>
 __device__ __forceinline__ void epilogue_staged(const Params& p, int bh, int row0, int lane,
                                                 float m, float l, const f32x16 (&o)[DB],
-                                                unsigned char* stage) {
+                                                unsigned char* stage, int col0 = 0,
+                                                bool lse = true) {
   typedef OutT v4 __attribute__((ext_vector_type(4)));
   constexpr int RB = D * 2, CPR = D / 8;  // bytes and 16-byte slots per row
   // Addresses come from an opaque copy of the lane index: computed here, not
@@ -548,9 +555,9 @@ __device__ __forceinline__ void epilogue_staged(const Params& p, int bh, int row
   for (int k = 0; k < 32 / RPI; ++k) {
     const int r = k * RPI + lane / CPR, c = lane % CPR;
     const i32x4 v = *(FA_LDS const i32x4*)(stage + r * RB + ((c ^ (r % CPR)) << 4));
-    if (row0 + r < p.N) *(i32x4*)((OutT*)p.o + ((size_t)bh * p.N + row0 + r) * D + 8 * c) = v;
+    if (row0 + r < p.N) *(i32x4*)((OutT*)p.o + ((size_t)bh * p.N + row0 + r) * DO + col0 + 8 * c) = v;
   }
-  if (hi == 0 && row0 + l32 < p.N)
+  if (lse && hi == 0 && row0 + l32 < p.N)
     p.lse[(size_t)bh * p.N + row0 + l32] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
 }
 
@@ -1150,7 +1157,11 @@ __device__ __forceinline__ To same_size_cast(const From& x) {
   else return To{};
 }
 
-template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8, bool VL = false>
+// DV < D (head dim 256): the workgroup owns columns [vh*DV, vh*DV + DV) of V
+// and O, vh = 0 .. D/DV - 1, and computes the whole S over all D dimensions;
+// the workgroups of one query tile reach the same reference maxima and sums
+// with no communication, and the first one writes LSE.
+template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8, bool VL = false, int DV = D>
 __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   using T = typename E::T;  // P, V in LDS and O (bfloat16 for fp8 inputs)
   using v8 = typename E::v8;
@@ -1159,38 +1170,46 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   static_assert(G == 1 || G == 2, "one or two 32-row groups per wave");
   static_assert(!F8 || (G == 1 && NB == 2), "fp8 inputs: one row group, two buffers");
   static_assert(!(F8 && VL), "packed batches take 16-bit inputs");
+  static_assert(DV == D || (!F8 && !VL && G == 1 && D % DV == 0), "column slices: 16-bit, one row group");
+  constexpr int NVH = D / DV;  // workgroups per query tile (column slices of V and O)
   constexpr int WR = 32 * G;   // query rows per wave
   constexpr int BR = NW * WR;  // query rows per workgroup
   constexpr int BC = 64;       // keys per LDS tile
   constexpr int KS = F8 ? D / 64 : D / 16;  // S MFMA steps over the head dim
-  constexpr int DB = D / 32;   // 32-wide head-dim blocks of O^T
-  constexpr int RB = D * 2;    // bytes per 16-bit V (and 16-bit K) row in LDS
+  constexpr int DB = DV / 32;  // 32-wide blocks of the O^T columns this workgroup owns
+  constexpr int RB = D * 2;    // bytes per 16-bit row in memory (and per 16-bit K row in LDS)
+  constexpr int VRB = DV * 2;  // bytes per V row (slice) in LDS
   constexpr int KRB = F8 ? D : RB;  // bytes per K row (global and LDS)
-  constexpr int CPR = D / 8;   // 16-byte slots per 16-bit row
+  constexpr int CPR = DV / 8;  // 16-byte slots per V row (slice) in LDS
   constexpr int KCPR = KRB / 16;    // 16-byte slots per K row
-  constexpr int TB = BC * RB;  // bytes per 16-bit tile (every LDS buffer's size)
+  constexpr int TB = BC * RB;  // bytes per K buffer
+  constexpr int TBV = BC * VRB;  // bytes per V buffer
   constexpr int NKC = BC * KRB / 1024;  // 1 KB copies per K tile
   constexpr int NDMA = (NKC + NW - 1) / NW;  // K copies per wave per tile (some idle when ragged)
+  constexpr int NVC = TBV / 1024;  // 1 KB copies per 16-bit V tile
+  constexpr int NDMAV = NVC / NW;  // V copies per wave per tile
   constexpr int NPV = 2 * DB;  // PV MFMA steps per half (2 x 16 keys)
   constexpr int LA = FA_PIPE_LOOKAHEAD;
   static_assert(F8 || NKC % NW == 0, "16-bit tiles must split into 1 KB copies per wave");
+  static_assert(F8 || NVC % NW == 0, "16-bit V tiles must split into 1 KB copies per wave");
   static_assert(NB >= 2 && NB <= 4, "two to four LDS buffers per operand");
 
   // One named array per buffer: distinct objects let the compiler see that a
   // copy in flight into one buffer cannot alias operand reads from another.
   constexpr int TB2 = NB > 2 ? TB : 16, TB3 = NB > 3 ? TB : 16;
+  constexpr int TBV2 = NB > 2 ? TBV : 16, TBV3 = NB > 3 ? TBV : 16;
   __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char k2s[TB2];
   __shared__ __attribute__((aligned(1024))) unsigned char k3s[TB3];
-  __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v2s[TB2];
-  __shared__ __attribute__((aligned(1024))) unsigned char v3s[TB3];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0s[TBV];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1s[TBV];
+  __shared__ __attribute__((aligned(1024))) unsigned char v2s[TBV2];
+  __shared__ __attribute__((aligned(1024))) unsigned char v3s[TBV3];
   // With the cross-item prefetch the next item's first tiles land in the K/V
   // buffers while this item's O is staged, so O gets a region of its own.
-  constexpr bool PF = FA_PIPE_PREFETCH && CAUSAL && !F8;
-  __shared__ __attribute__((aligned(1024))) unsigned char ostage[PF ? NW * G * 32 * D * 2 : 16];
+  constexpr bool PF = FA_PIPE_PREFETCH && CAUSAL && !F8 && DV == D;
+  __shared__ __attribute__((aligned(1024))) unsigned char ostage[PF ? NW * G * 32 * DV * 2 : 16];
   auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* {
     return i == 0 ? k0s : i == 1 ? k1s : i == 2 ? k2s : k3s;
   };
@@ -1210,13 +1229,17 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // through its L2. The middle tile of an odd n_qt is one workgroup's only
   // tile.
   const int units = CAUSAL ? (p.n_qt + 1) / 2 : p.n_qt;
-  int bh, u;
+  int bh, u, vh = 0;
   if constexpr (VL) {
     varlen_item(p.H, units, bh, u);
   } else {
     const int bid = blockIdx.x, total = gridDim.x;
     int logical = bid;
     if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+    if constexpr (NVH > 1) {  // the column slices of a unit are consecutive (one XCD)
+      vh = logical % NVH;
+      logical /= NVH;
+    }
     bh = logical / units;
     u = logical - bh * units;
   }
@@ -1280,14 +1303,14 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int c = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
-      voff[db] = r * RB + ((c ^ v_swz<D>(r)) << 4) + 8 * (i & 1);
+      voff[db] = r * VRB + ((c ^ v_swz<DV>(r)) << 4) + 8 * (i & 1);
     }
   }
   const RowRange rr = row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
   const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;  // elements
   const unsigned char* Qh = (const unsigned char*)p.q + head * (KRB / D);
   const unsigned char* Kh = (const unsigned char*)p.k + kv_head * (KRB / D);
-  const unsigned char* Vh = (const unsigned char*)p.v + kv_head * (KRB / D);
+  const unsigned char* Vh = (const unsigned char*)p.v + kv_head * (KRB / D) + vh * VRB;
 
   (void)Qh;
   if (!(PF && prefetched)) load_q(rr);
@@ -1302,28 +1325,32 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   auto copy_tile_with = [&](__amdgpu_buffer_rsrc_t rs, int j, unsigned char* dst, auto is_v)
       __attribute__((always_inline)) {
     constexpr bool IV = decltype(is_v)::value;
+    // rb: bytes per row in memory; an LDS row holds cpr 16-byte slots
     constexpr int cpr = IV ? CPR : KCPR, rb = IV ? RB : KRB;
+    constexpr int nd = IV ? NDMAV : NDMA, nc = IV ? NVC : NKC;
 #pragma unroll
-    for (int c = 0; c < NDMA; ++c) {
+    for (int c = 0; c < nd; ++c) {
       const int blk = c * NW + wave;
-      if (NKC % NW == 0 || blk < NKC) {
+      if (nc % NW == 0 || blk < nc) {
         const int slot = blk * 64 + lane;
         const int r = slot / cpr, ps = slot % cpr;
-        const int lc = ps ^ (IV ? v_swz<D>(r) : F8 ? k8_swz<D>(r) : k_swz<D>(r));
+        const int lc = ps ^ (IV ? v_swz<DV>(r) : F8 ? k8_swz<D>(r) : k_swz<D>(r));
         lds_copy16(rs, dst + blk * 1024, j * (BC * rb) + r * rb + (lc << 4));
       }
     }
   };
   auto copy_tile = [&](int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
     constexpr bool IV = decltype(is_v)::value;
+    // rb: bytes per row in memory; an LDS row holds cpr 16-byte slots
     constexpr int cpr = IV ? CPR : KCPR, rb = IV ? RB : KRB;
+    constexpr int nd = IV ? NDMAV : NDMA, nc = IV ? NVC : NKC;
 #pragma unroll
-    for (int c = 0; c < NDMA; ++c) {
+    for (int c = 0; c < nd; ++c) {
       const int blk = c * NW + wave;
-      if (NKC % NW == 0 || blk < NKC) {
+      if (nc % NW == 0 || blk < nc) {
         const int slot = blk * 64 + lane;
         const int r = slot / cpr, ps = slot % cpr;
-        const int lc = ps ^ (IV ? v_swz<D>(r) : F8 ? k8_swz<D>(r) : k_swz<D>(r));
+        const int lc = ps ^ (IV ? v_swz<DV>(r) : F8 ? k8_swz<D>(r) : k_swz<D>(r));
         lds_copy16(IV ? rsV : rsK, dst + blk * 1024, j * (BC * rb) + r * rb + (lc << 4));
       }
     }
@@ -1361,10 +1388,10 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   };
   // V^T operand of PV step u = ps*DB + db over keys 32*h + 16*ps + [0, 16)
   auto vfrag = [&](const unsigned char* vb, int h, int u) __attribute__((always_inline)) {
-    const unsigned char* b = vb + (32 * h + 16 * (u / DB)) * RB + voff[u % DB];
+    const unsigned char* b = vb + (32 * h + 16 * (u / DB)) * VRB + voff[u % DB];
     const v4 a0 = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)b));
     const v4 a1 =
-        __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
+        __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * VRB)));
     return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // S^T = K Q^T over one 32-key half for every group, each K operand read once
@@ -1610,7 +1637,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // end of iteration t only the copies of the last NB-2 iterations may still
   // be in flight. Copies past the end have an empty byte range and move
   // nothing, which keeps those counts exact.
-  constexpr int KEEP = (NB - 2) * 2 * NDMA;
+  constexpr int KEEP = (NB - 2) * (NDMA + NDMAV);
   // fp8 V tiles take registers instead: loaded with the copies, stored to
   // vx just before the iteration's barrier.
   auto copies = [&](int t, unsigned char* kx, unsigned char* vx) __attribute__((always_inline)) {
@@ -1697,14 +1724,15 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
       }
     }
   }
-  static_assert(NW * G <= 8 && TB >= 2 * 32 * D * 2, "O staging space");
+  static_assert(NW * G <= 8 && TB >= 2 * 32 * DV * 2 && TBV >= 2 * 32 * DV * 2, "O staging space");
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int slot = wave * G + g;
-    unsigned char* stage = PF ? ostage + slot * (32 * D * 2)
+    unsigned char* stage = PF ? ostage + slot * (32 * DV * 2)
                               : (slot < 2 ? k0s : slot < 4 ? k1s : slot < 6 ? v0s : v1s) +
-                                    (slot & 1) * (32 * D * 2);
-    epilogue_staged<T, D, DB>(p, rr.bh, rr.qw0 + 32 * g, lane, m[g], l[g], o[g], stage);
+                                    (slot & 1) * (32 * DV * 2);
+    epilogue_staged<T, DV, DB, D>(p, rr.bh, rr.qw0 + 32 * g, lane, m[g], l[g], o[g], stage, vh * DV,
+                                  vh == 0);
   }
   // staging reads done before the next tile's copies land (a region of its
   // own with the prefetch: each wave only ever reuses its own slice)
@@ -2883,7 +2911,10 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
 }  // namespace
 
 int rows_per_block(Kind kind, int d, int N, bool causal, bool window) {
-  if (d == 256) return (kind == Kind::BF16 || kind == Kind::F16) && !window ? 4 * 32 : 0;
+  if (d == 256) {
+    if ((kind != Kind::BF16 && kind != Kind::F16) || window) return 0;
+    return FA_D256_PIPE && use_pipe(N, causal) ? FA_WIDE_WAVES * 32 : 4 * 32;
+  }
   if (d != 64 && d != 128) return 0;
   if (window) return (kind == Kind::BF16 || kind == Kind::F16) ? FA_DMA_WAVES * 32 : 0;
   if (kind == Kind::FP8 && use_pipe(N, causal)) return FA_WIDE_WAVES * 32;
@@ -2898,6 +2929,19 @@ int rows_per_block(Kind kind, int d, int N, bool causal, bool window) {
 
 hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream) {
   if (d == 256) {
+#if FA_D256_PIPE
+    // the pipelined kernel on 128-column slices of V and O (two workgroups
+    // per query tile, or per folded pair of causal tiles)
+    if ((kind == Kind::BF16 || kind == Kind::F16) && use_pipe(p.N, causal)) {
+      const int units = 2 * (causal ? (p.n_qt + 1) / 2 : p.n_qt);
+      constexpr int T = FA_WIDE_WAVES * 64;
+      if (kind == Kind::BF16)
+        return causal ? launch(attn_fwd_pipe<Bf16, 256, 1, FA_WIDE_WAVES, 2, true, false, false, 128>, p, T, stream, units)
+                      : launch(attn_fwd_pipe<Bf16, 256, 1, FA_WIDE_WAVES, 2, false, false, false, 128>, p, T, stream, units);
+      return causal ? launch(attn_fwd_pipe<F16, 256, 1, FA_WIDE_WAVES, 2, true, false, false, 128>, p, T, stream, units)
+                    : launch(attn_fwd_pipe<F16, 256, 1, FA_WIDE_WAVES, 2, false, false, false, 128>, p, T, stream, units);
+    }
+#endif
     // two workgroups (column halves of O) per query tile
     const long long grid = 2LL * p.B * p.H * p.n_qt;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;

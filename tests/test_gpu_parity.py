@@ -165,7 +165,8 @@ def test_named_workload_full_oracle(name):
     assert_close(o, lse, o_ref, lse_ref, w.spec.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["long_causal_bf16", "long_causal_fp8", "long_causal_grouped_bf16"])
+@pytest.mark.parametrize("name", ["long_causal_bf16", "long_causal_fp8", "long_causal_grouped_bf16",
+                                  "long_causal_d256_bf16"])
 def test_named_workload_sampled_rows(name):
     """Full-size long-context workloads: every head, sampled rows (tile edges,
     the outlier keys' own rows, random rows) against the oracle row by row."""
@@ -223,7 +224,9 @@ def test_grouped_kv_heads(dtype, d, N, causal, padded, H, H_kv):
 # Head dimension 256 (16-bit inputs): two workgroups per query tile, one per
 # column half of O; ragged tiles, padding, grouped heads and a longer sequence.
 D256 = [(1, False, 2, 2, 2), (33, True, 2, 3, 3), (127, False, 1, 4, 2), (300, True, 2, 2, 1),
-        (1000, False, 1, 2, 2)]
+        (1000, False, 1, 2, 2),
+        # long enough for the pipelined kernel's column slices with a causal mask
+        (4160, False, 1, 2, 1), (4097, True, 1, 2, 2)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
