@@ -2179,10 +2179,13 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 #define FA_BWD_KV_OCC 2  // waves per SIMD the dK/dV pass is compiled for (1: 512 registers)
 #endif
 #ifndef FA_BWD_FENCE
-// backward passes: operand reads held ahead of their products by scheduling
+// dK/dV pass: operand reads held ahead of their products by scheduling
 // fences, FA_BWD_FENCE_LA products ahead (0: the compiler places the reads,
 // FA_BWD_LOOKAHEAD ahead in program order)
 #define FA_BWD_FENCE 0
+#endif
+#ifndef FA_BWD_DQ_FENCE
+#define FA_BWD_DQ_FENCE 0  // the same fences for the dQ pass alone (FA_BWD_FENCE: the dK/dV pass)
 #endif
 #ifndef FA_BWD_FENCE_LA
 #define FA_BWD_FENCE_LA 1
@@ -2522,16 +2525,18 @@ struct SwzTile {
   __device__ __forceinline__ int row(int c) const { return roff + ((c ^ sw) << 4); }
 };
 
-constexpr int kBwdLA = FA_BWD_FENCE ? FA_BWD_FENCE_LA : FA_BWD_LOOKAHEAD;
+// FN: operand reads held ahead of their products by fences (operand_fence).
+template <bool FN>
+constexpr int bwd_la() { return FN ? FA_BWD_FENCE_LA : FA_BWD_LOOKAHEAD; }
 
 // acc^T[n][col] += sum_k Y[k][n] * M[k][col] over the 32 rows k of a swizzled
 // tile Y, M given as the packed 16-bit operand of a D-layout accumulator.
-template <class E, int D>
+template <class E, int D, bool FN>
 __device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzTile<D>& sz,
                                            const typename E::v8 (&m)[2], f32x16 (&acc)[D / 32]) {
   using v4 = typename E::v4;
   using v8 = typename E::v8;
-  constexpr int DB = D / 32, RB = D * 2, LA = kBwdLA;
+  constexpr int DB = D / 32, RB = D * 2, LA = bwd_la<FN>();
   v8 ring[LA + 1];
 #pragma unroll
   for (int t = 0; t < 2 * DB + LA; ++t) {
@@ -2541,33 +2546,33 @@ __device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzT
       const v4 a1 = __builtin_bit_cast(
           v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
       ring[t % (LA + 1)] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-      if constexpr (FA_BWD_FENCE) operand_fence();
+      if constexpr (FN) operand_fence();
     }
     const int u = t - LA;
     if (u >= 0) {
       acc[u % DB] = E::mma(ring[u % (LA + 1)], m[u / DB], acc[u % DB]);
-      if constexpr (FA_BWD_FENCE) operand_fence();
+      if constexpr (FN) operand_fence();
     }
   }
 }
 
 // S = X Y^T alone (as two_products without the second product).
-template <class E, int D>
+template <class E, int D, bool FN>
 __device__ __forceinline__ void one_product(const unsigned char* x, const SwzTile<D>& sz, int hi,
                                             const typename E::v8 (&y)[D / 16], f32x16& s) {
   using v8 = typename E::v8;
-  constexpr int KS = D / 16, LA = kBwdLA;
+  constexpr int KS = D / 16, LA = bwd_la<FN>();
   v8 ra[LA + 1];
 #pragma unroll
   for (int t = 0; t < KS + LA; ++t) {
     if (t < KS) {
       ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
-      if constexpr (FA_BWD_FENCE) operand_fence();
+      if constexpr (FN) operand_fence();
     }
     const int u = t - LA;
     if (u >= 0) {
       s = E::mma(ra[u % (LA + 1)], y[u], s);
-      if constexpr (FA_BWD_FENCE) operand_fence();
+      if constexpr (FN) operand_fence();
     }
   }
 }
@@ -2575,27 +2580,27 @@ __device__ __forceinline__ void one_product(const unsigned char* x, const SwzTil
 // S = X Y^T and dP = Z W^T over the head dim for one 32-row tile: X, Z rows
 // of swizzled LDS tiles (A operands), Y, W in registers (B operands); operand
 // reads issued FA_BWD_LOOKAHEAD steps ahead.
-template <class E, int D>
+template <class E, int D, bool FN>
 __device__ __forceinline__ void two_products(const unsigned char* x, const unsigned char* z,
                                              const SwzTile<D>& sz, int hi,
                                              const typename E::v8 (&y)[D / 16],
                                              const typename E::v8 (&w)[D / 16], f32x16& s,
                                              f32x16& dp) {
   using v8 = typename E::v8;
-  constexpr int KS = D / 16, LA = kBwdLA;
+  constexpr int KS = D / 16, LA = bwd_la<FN>();
   v8 ra[LA + 1], rb[LA + 1];
 #pragma unroll
   for (int t = 0; t < KS + LA; ++t) {
     if (t < KS) {
       ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
       rb[t % (LA + 1)] = *(const v8*)(z + sz.row(2 * t + hi));
-      if constexpr (FA_BWD_FENCE) operand_fence();
+      if constexpr (FN) operand_fence();
     }
     const int u = t - LA;
     if (u >= 0) {
       s = E::mma(ra[u % (LA + 1)], y[u], s);
       dp = E::mma(rb[u % (LA + 1)], w[u], dp);
-      if constexpr (FA_BWD_FENCE) operand_fence();
+      if constexpr (FN) operand_fence();
     }
   }
 }
@@ -2687,7 +2692,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
     auto tile = [&](auto masked) __attribute__((always_inline)) {
       f32x16 s[1] = {f32x16{}};
       f32x16 dp = {};
-      two_products<E, D>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
+      two_products<E, D, FA_BWD_DQ_FENCE>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
       if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
       v8 ds[2];
 #pragma unroll
@@ -2698,7 +2703,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
           const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
           ds[ps][e] = E::cvt(pr * (dp[i] - dl));
         }
-      tr_product<E, D>(kb[buf], sz, ds, dq);
+      tr_product<E, D, FA_BWD_DQ_FENCE>(kb[buf], sz, ds, dq);
     };
     if (j < wfull) tile(std::false_type{});
     else if (j < wnt) tile(std::true_type{});
@@ -2804,8 +2809,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     copies(u + 2, (u + 2) % kBwdBufs);
     if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
       f32x16 s = {}, dp = {};
-      if constexpr (MODE == 1) one_product<E, D>(qb[buf], sz, hi, kf, s);
-      else two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
+      if constexpr (MODE == 1) one_product<E, D, FA_BWD_FENCE>(qb[buf], sz, hi, kf, s);
+      else two_products<E, D, FA_BWD_FENCE>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
       v8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -2821,8 +2826,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
           if constexpr (MODE != 1) dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
         }
       }
-      if constexpr (MODE != 2) tr_product<E, D>(ob[buf], sz, pf, dv);
-      if constexpr (MODE != 1) tr_product<E, D>(qb[buf], sz, dsf, dk);
+      if constexpr (MODE != 2) tr_product<E, D, FA_BWD_FENCE>(ob[buf], sz, pf, dv);
+      if constexpr (MODE != 1) tr_product<E, D, FA_BWD_FENCE>(qb[buf], sz, dsf, dk);
     }
     wait_vmem_keep<2 * NCPW>();  // row stats u+1 and tile u+1 landed; tile u+2 may be in flight
     if (tid < 32) ls[nbuf][tid] = lreg, dls[nbuf][tid] = dlreg;
