@@ -112,6 +112,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_DMA_FENCE
 #define FA_DMA_FENCE 1  // direct-to-LDS kernel: operand reads held FA_LOOKAHEAD products ahead by fences
 #endif
+#ifndef FA_WIN_PIPE
+#define FA_WIN_PIPE 0  // sliding windows on the pipelined kernel where it would take the unbanded case
+#endif
 #ifndef FA_D256_PIPE
 #define FA_D256_PIPE 1  // head dim 256 on the pipelined kernel (column slices) where d = 128 takes it
 #endif
@@ -1161,7 +1164,9 @@ __device__ __forceinline__ To same_size_cast(const From& x) {
 // and O, vh = 0 .. D/DV - 1, and computes the whole S over all D dimensions;
 // the workgroups of one query tile reach the same reference maxima and sums
 // with no communication, and the first one writes LSE.
-template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8, bool VL = false, int DV = D>
+// WIN: banded mask (window) on top of the causal and padding masks.
+template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8, bool VL = false, int DV = D,
+          bool WIN = false>
 __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   using T = typename E::T;  // P, V in LDS and O (bfloat16 for fp8 inputs)
   using v8 = typename E::v8;
@@ -1171,6 +1176,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   static_assert(!F8 || (G == 1 && NB == 2), "fp8 inputs: one row group, two buffers");
   static_assert(!(F8 && VL), "packed batches take 16-bit inputs");
   static_assert(DV == D || (!F8 && !VL && G == 1 && D % DV == 0), "column slices: 16-bit, one row group");
+  static_assert(!WIN || (!F8 && !VL && DV == D), "windows: 16-bit inputs, whole rows");
   constexpr int NVH = D / DV;  // workgroups per query tile (column slices of V and O)
   constexpr int WR = 32 * G;   // query rows per wave
   constexpr int BR = NW * WR;  // query rows per workgroup
@@ -1208,7 +1214,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char v3s[TBV3];
   // With the cross-item prefetch the next item's first tiles land in the K/V
   // buffers while this item's O is staged, so O gets a region of its own.
-  constexpr bool PF = FA_PIPE_PREFETCH && CAUSAL && !F8 && DV == D;
+  constexpr bool PF = FA_PIPE_PREFETCH && CAUSAL && !F8 && DV == D && !WIN;
   __shared__ __attribute__((aligned(1024))) unsigned char ostage[PF ? NW * G * 32 * DV * 2 : 16];
   auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* {
     return i == 0 ? k0s : i == 1 ? k1s : i == 2 ? k2s : k3s;
@@ -1306,11 +1312,38 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
       voff[db] = r * VRB + ((c ^ v_swz<DV>(r)) << 4) + 8 * (i & 1);
     }
   }
-  const RowRange rr = row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
+  RowRange rr = row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
+  // Sliding window: the workgroup streams key tiles from t0, the first tile
+  // any of its rows may see, counted from there: the K/V bases move t0 tiles
+  // on, so the tile indices, buffers and loop bounds below are relative to t0
+  // and kbase is the first key of tile 0. A wave's tiles before whead hold
+  // keys below the band of some of its rows and take the mask.
+  int kbase = 0, whead = 0;
+  if constexpr (WIN) {
+    const int wl = p.win_left, wr = p.win_right;
+    int t0 = 0;
+    if (wl >= 0) {
+      t0 = max(0, rr.q_wg0 - wl) / BC;
+      whead = (max(0, rr.qw0 + WR - 1 - wl) + BC - 1) / BC;
+    }
+    if (wr >= 0) {
+      rr.nt = min(rr.nt, (min(rr.kl, rr.q_wg0 + BR + wr) + BC - 1) / BC);
+      rr.wnt = min(rr.wnt, (max(0, min(rr.kl, rr.qw0 + WR + wr)) + BC - 1) / BC);
+      rr.wfull = min(rr.wfull, max(0, rr.qw0 + wr + 1) / BC);
+    }
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    kbase = t0 * BC;
+    rr.nt -= t0;
+    rr.wnt -= t0;
+    rr.wfull -= t0;
+    whead = __builtin_amdgcn_readfirstlane(whead - t0);
+  }
   const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;  // elements
   const unsigned char* Qh = (const unsigned char*)p.q + head * (KRB / D);
-  const unsigned char* Kh = (const unsigned char*)p.k + kv_head * (KRB / D);
-  const unsigned char* Vh = (const unsigned char*)p.v + kv_head * (KRB / D) + vh * VRB;
+  const unsigned char* Kh = (const unsigned char*)p.k + (kv_head + (size_t)kbase * D) * (KRB / D);
+  const unsigned char* Vh =
+      (const unsigned char*)p.v + (kv_head + (size_t)kbase * D) * (KRB / D) + vh * VRB;
+  const int kvl = WIN ? max(0, rr.kl - kbase) : rr.kl;  // valid key rows from tile 0 on
 
   (void)Qh;
   if (!(PF && prefetched)) load_q(rr);
@@ -1318,8 +1351,8 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // host keeps a head under 1 GiB): a tile's copy only adds its byte offset,
   // and rows at or beyond kl (a ragged last tile, tiles past the end) read
   // as zeros.
-  const auto rsK = buffer_rsrc(Kh, rr.kl * KRB);
-  const auto rsV = buffer_rsrc(Vh, rr.kl * KRB);
+  const auto rsK = buffer_rsrc(Kh, kvl * KRB);
+  const auto rsV = buffer_rsrc(Vh, kvl * KRB);
   // K tile j (and V tile j for 16-bit inputs) straight into LDS, 16-byte
   // slots permuted per row as the operand reads expect.
   auto copy_tile_with = [&](__amdgpu_buffer_rsrc_t rs, int j, unsigned char* dst, auto is_v)
@@ -1438,6 +1471,12 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
         for (int g = 0; g < G; ++g) o[g][u % DB] = E::mma(ring[u % (LA + 1)], pf[g][u / DB], o[g][u % DB]);
     }
   };
+  // The masks of one half (its first key k0) for query row qrow.
+  auto mask_half = [&](f32x16& sh, int k0, int qrow) __attribute__((always_inline)) {
+    auto& s1 = *reinterpret_cast<f32x16(*)[1]>(&sh);
+    if constexpr (WIN) apply_mask_window<1, CAUSAL>(s1, k0, rr.kl, qrow, hi, p.win_left, p.win_right);
+    else apply_mask<1, CAUSAL>(s1, k0, rr.kl, qrow, hi);
+  };
   // P of one half from its raw scores s (k0 = its first key); updates l and,
   // on the rare branch, m, base and O.
   // The rare branch of probs: move the reference maxima of the rows of this
@@ -1474,7 +1513,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if constexpr (decltype(masked)::value)
-        apply_mask<1, CAUSAL>(*reinterpret_cast<f32x16(*)[1]>(&s[g]), k0, rr.kl, rr.qrow + 32 * g, hi);
+        mask_half(s[g], k0, rr.qrow + 32 * g);
       rs[g] = 0.0f;
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps) {
@@ -1552,7 +1591,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         if constexpr (decltype(masked)::value)
-          apply_mask<1, CAUSAL>(*reinterpret_cast<f32x16(*)[1]>(&s_in[g]), k0, rr.kl, rr.qrow + 32 * g, hi);
+          mask_half(s_in[g], k0, rr.qrow + 32 * g);
         rs[g] = 0.0f;
       }
     }
@@ -1614,22 +1653,22 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next,
                        auto mask_a, auto mask_b) __attribute__((always_inline)) {
     if constexpr (FA_PIPE_FENCE == 2 && !F8) {
-      unit(kb, 0, sa, vb, pfa, sb, pfb, BC * t + 32, has_next, mask_a, std::true_type{});
-      unit(kb, 1, sb, vb, pfb, sa, pfa, BC * (t + 1), has_next, mask_b, has_next);
+      unit(kb, 0, sa, vb, pfa, sb, pfb, kbase + BC * t + 32, has_next, mask_a, std::true_type{});
+      unit(kb, 1, sb, vb, pfb, sa, pfa, kbase + BC * (t + 1), has_next, mask_b, has_next);
       return;
     }
     if constexpr (FA_PIPE_FENCE && !F8) {
       mma_half(kb, 0, sa, vb, pfa, has_next);
-      probs(sb, pfb, BC * t + 32, mask_a);
+      probs(sb, pfb, kbase + BC * t + 32, mask_a);
       mma_half(kb, 1, sb, vb, pfb, has_next);
     } else {
       if constexpr (decltype(has_next)::value) scores(kb, 0, sa);
       pv(vb, 0, pfa);
-      probs(sb, pfb, BC * t + 32, mask_a);
+      probs(sb, pfb, kbase + BC * t + 32, mask_a);
       if constexpr (decltype(has_next)::value) scores(kb, 1, sb);
       pv(vb, 1, pfb);
     }
-    if constexpr (decltype(has_next)::value) probs(sa, pfa, BC * (t + 1), mask_b);
+    if constexpr (decltype(has_next)::value) probs(sa, pfa, kbase + BC * (t + 1), mask_b);
   };
   // K tile j lives in buffer j % NB, V tile j in buffer j % NB. Iteration t
   // reads K t+1 and V t and refills the buffers of K t (with K t+NB) and of
@@ -1669,14 +1708,32 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   if (rr.wnt > 0) {
     scores(k0s, 0, sa);
     scores(k0s, 1, sb);
-    if (0 < rr.wfull) probs(sa, pfa, 0, std::false_type{});
-    else probs(sa, pfa, 0, std::true_type{});
+    if (0 < rr.wfull && (!WIN || 0 >= whead)) probs(sa, pfa, kbase, std::false_type{});
+    else probs(sa, pfa, kbase, std::true_type{});
   }
   __syncthreads();  // K of tile 0 is read by every wave before its buffer is refilled
   // Iterations [0, ts): every half unmasked and a next tile to score; NB of
   // them per pass so that every buffer is named at compile time.
   const int ts = max(0, rr.wfull - 1);
   int t = 0;
+  if constexpr (WIN) {
+    // The wave's masked head, in whole passes of NB iterations so that the
+    // steady loop starts on buffer 0 (every wave still takes one barrier per
+    // tile, whatever its head's length).
+    const int hs = min(rr.nt, (max(0, whead) + NB - 1) / NB * NB);
+    for (; t < hs; ++t) {
+      const int q = t % NB;
+      unsigned char* kb = kbuf(q + 1 == NB ? 0 : q + 1);
+      unsigned char* vb = vbuf(q);
+      unsigned char* vx = vbuf(q == 0 ? NB - 1 : q - 1);
+      copies(t, kbuf(q), vx);
+      if (t < rr.wnt) {
+        if (t + 1 < rr.wnt) iteration(t, kb, vb, std::true_type{}, std::true_type{}, std::true_type{});
+        else iteration(t, kb, vb, std::false_type{}, std::true_type{}, std::false_type{});
+      }
+      sync_after(vx);
+    }
+  }
   for (; t + NB <= ts; t += NB) {
     static_for<NB>([&](auto P) __attribute__((always_inline)) {
       constexpr int q = decltype(P)::value;
@@ -2872,9 +2929,13 @@ bool use_pipe(int N, bool causal) {
 
 template <class E, int D, bool C>
 hipError_t launch_16bit(const Params& p, hipStream_t s) {
-  if (p.win_left >= 0 || p.win_right >= 0)
+  if (p.win_left >= 0 || p.win_right >= 0) {
+    if (FA_WIN_PIPE && use_pipe(p.N, C))
+      return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false, false, D, true>,
+                    p, FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
     return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C, true>, p,
                   FA_DMA_WAVES * 64, s);
+  }
   if (use_pipe(p.N, C))
     return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false>, p,
                   FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
@@ -2921,7 +2982,10 @@ int rows_per_block(Kind kind, int d, int N, bool causal, bool window) {
     return FA_D256_PIPE && use_pipe(N, causal) ? FA_WIDE_WAVES * 32 : 4 * 32;
   }
   if (d != 64 && d != 128) return 0;
-  if (window) return (kind == Kind::BF16 || kind == Kind::F16) ? FA_DMA_WAVES * 32 : 0;
+  if (window) {
+    if (kind != Kind::BF16 && kind != Kind::F16) return 0;
+    return FA_WIN_PIPE && use_pipe(N, causal) ? FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS : FA_DMA_WAVES * 32;
+  }
   if (kind == Kind::FP8 && use_pipe(N, causal)) return FA_WIDE_WAVES * 32;
   if (kind == Kind::BF16 || kind == Kind::F16) {
     if (use_pipe(N, causal)) return FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS;

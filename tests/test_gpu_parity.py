@@ -243,6 +243,64 @@ def test_head_dim_256(dtype, causal):
         assert_close(o, lse, o_ref, lse_ref, dtype, f"d256 N={N}")
 
 
+# Windows over sequences long enough for the pipelined kernel (causal N >= 4096;
+# every non-causal length takes it): bands narrower and wider than its 256-row
+# query tiles, a band of zero width, a two-sided band, padding and grouped heads.
+LONG_WINDOWS = [  # causal, (left, right), N, padded, H_kv
+    (True, (100, -1), 4160, False, 2), (True, (1000, -1), 4097, True, 1), (True, (0, -1), 4096, False, 2),
+    (True, (300, 5), 4160, True, 2), (False, (130, 0), 4160, False, 1), (False, (40, 700), 4100, True, 2)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_sliding_window_long(dtype, d):
+    for i, (causal, window, N, padded, H_kv) in enumerate(LONG_WINDOWS):
+        spec = small_spec(dtype, d, N, causal, padded, B=1, H=2,
+                          seed=9950 + 7 * i + d).with_shape(H_kv=H_kv)
+        say(f"case long window dtype={dtype} d={d} causal={causal} window={window} N={N} "
+            f"padded={padded} H_kv={H_kv} seed={spec.seed}")
+        w = W.draw(spec)
+        q, k, v, kl = to_device(w)
+        o, lse = fa.fwd(q, k, v, scale=spec.scale, causal=causal, key_len=kl, window=window)
+        torch.cuda.synchronize()
+        qe, ke, ve = w.exact()
+        o_ref, lse_ref = oracle.attention_forward(qe, ke, ve, spec.scale, causal,
+                                                  w.key_len_or_none(), window=window)
+        assert_close(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref,
+                     dtype, f"window={window} N={N}")
+
+
+def test_window_workload_sampled_rows():
+    """The full-size sliding-window workload: every head, sampled rows
+    (tile edges, band edges, random rows) against the oracle row by row."""
+    w = W.draw(W.SPECS["long_causal_window_bf16"])
+    s = w.spec
+    window = (s.window_left, -1)
+    say(f"case long_causal_window_bf16 sampled rows seed={s.seed}")
+    q, k, v, kl = to_device(w)
+    o, lse = fa.fwd(q, k, v, scale=s.scale, causal=s.causal, key_len=kl, window=window)
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    qe, ke, ve = w.exact()
+    rng = np.random.default_rng(s.seed + 1)
+    errs_o, errs_l = [], []
+    for h in range(s.H):
+        edges = [s.window_left - 1, s.window_left, s.window_left + 1, 255, 256, 257, s.N - 1]
+        rows = sorted(set(edges) | set(rng.integers(0, s.N, 16).tolist()))
+        o_ref, lse_ref = oracle.attention_rows(qe, ke, ve, s.scale, s.causal, w.key_len_or_none(),
+                                               0, h, rows, window=window)
+        errs_o.append(o[0, h, rows] - o_ref)
+        errs_l.append(lse[0, h, rows] - lse_ref)
+    eo = np.abs(np.concatenate(errs_o))
+    el = np.abs(np.concatenate(errs_l))
+    from parity import TOL
+    t = TOL[s.dtype]
+    say(f"  window workload: rows={eo.shape[0]} max|dO|={eo.max():.3e} mean|dO|={eo.mean():.3e} "
+        f"max|dLSE|={el.max():.3e}")
+    assert np.all(np.isfinite(o))
+    assert eo.max() <= t["max_o"] and eo.mean() <= t["mean_o"] and el.max() <= t["lse"]
+
+
 # Sliding windows (fa_fwd_window): bands on either side, with and without the
 # causal mask, ragged lengths, padding and grouped heads.
 WINDOWS = [  # causal, (left, right)
