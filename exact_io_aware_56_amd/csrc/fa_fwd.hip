@@ -2244,6 +2244,15 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 #ifndef FA_BWD_DQ_FENCE
 #define FA_BWD_DQ_FENCE 0  // the same fences for the dQ pass alone (FA_BWD_FENCE: the dK/dV pass)
 #endif
+#ifndef FA_BWD_DQ_PIPE
+#define FA_BWD_DQ_PIPE 0  // dQ pass with the next key tile's products under this tile's dS work
+#endif
+#ifndef FA_BWD_DQ_PIPE_FENCE
+#define FA_BWD_DQ_PIPE_FENCE 1  // its operand reads held one product ahead by fences
+#endif
+#ifndef FA_BWD_DQ_PIPE_OCC
+#define FA_BWD_DQ_PIPE_OCC 1  // waves per SIMD it is compiled for (1: 512 registers)
+#endif
 #ifndef FA_BWD_FENCE_LA
 #define FA_BWD_FENCE_LA 1
 #endif
@@ -2771,6 +2780,123 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
 }
 
+// The dQ pass with the forward's cross-tile overlap: in iteration j the S and
+// dP products of key tile j+1 are issued among the vector instructions that
+// turn tile j's S and dP into dS, and dQ += dS K of tile j follows. Tiles j
+// and j+1 are resident (three buffers; the copy of tile j+2 goes into the
+// buffer of tile j-1) and each copy lands within the iteration it is issued
+// in. Two register sets for S and dP alternate between even and odd tiles.
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_DQ_PIPE_OCC) void attn_bwd_dq_pipe(BwdParams p) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char kb[kBwdBufs][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb[kBwdBufs][TB];
+  static_assert(kBwdBufs == 3, "tiles j and j+1 resident while tile j+2 is copied");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int N = p.N;
+  const int bh = blockIdx.x / p.n_qt;
+  const int qt = p.n_qt - 1 - (blockIdx.x - bh * p.n_qt);
+  const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
+  int kl = N;
+  if (p.key_len != nullptr) {
+    const int x = p.key_len[b];
+    kl = x < 0 ? 0 : (x > N ? N : x);
+  }
+  kl = __builtin_amdgcn_readfirstlane(kl);
+  const int q_wg0 = qt * kBwdRows, qw0 = q_wg0 + 32 * wave, qrow = qw0 + l32;
+  int kv_end = kl;
+  if (CAUSAL) kv_end = min(kv_end, min(N, q_wg0 + kBwdRows));
+  const int nt = (kv_end + 31) / 32;
+  int w_end = CAUSAL ? min(kv_end, qw0 + 32) : kv_end;
+  if (qw0 >= N) w_end = 0;
+  const int wnt = (w_end + 31) / 32;
+  int wfull = kl / 32;
+  if (CAUSAL) wfull = min(wfull, (qw0 + 1) / 32);
+  wfull = min(wfull, wnt);
+
+  const size_t head = (size_t)bh * N * D, kv_head = (size_t)kvh * N * D;
+  const T* Kh = (const T*)p.k + kv_head;
+  const T* Vh = (const T*)p.v + kv_head;
+  v8 qf[KS], df[KS];
+  {
+    const auto rq = tile_rsrc((const T*)p.q + head, 0, N, N, D * 2);
+    const auto rd = tile_rsrc((const T*)p.dout + head, 0, N, N, D * 2);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      qf[st] = __builtin_bit_cast(v8, load16(rq, qrow * D * 2 + 32 * st + 16 * hi));
+      df[st] = __builtin_bit_cast(v8, load16(rd, qrow * D * 2 + 32 * st + 16 * hi));
+    }
+  }
+  const bool row_ok = qrow < N;
+  const float lse2 = row_ok ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
+  const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.0f;
+  const float c = p.c;
+  SwzTile<D> sz;
+  sz.init(pinned_int(lane));
+
+  auto copies = [&](int j) __attribute__((always_inline)) {
+    const int buf = j % kBwdBufs;
+    copy_rows_swz<D>(Kh, j, kv_end, kb[buf], wave, lane);
+    copy_rows_swz<D>(Vh, j, kv_end, vb[buf], wave, lane);
+  };
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  f32x16 sa[1], dpa, sb[1], dpb;
+  // S and dP of tile j into (s, dp)
+  auto products = [&](int j, f32x16 (&s)[1], f32x16& dp) __attribute__((always_inline)) {
+    s[0] = f32x16{};
+    dp = f32x16{};
+    two_products<E, D, FA_BWD_DQ_PIPE_FENCE>(kb[j % kBwdBufs], vb[j % kBwdBufs], sz, hi, qf, df, s[0], dp);
+  };
+  // dS of tile j from its S and dP (masked when the tile needs it), then
+  // the next tile's products (when it has one) and dQ += dS K of tile j.
+  auto iteration = [&](int j, f32x16 (&s)[1], f32x16& dp, f32x16 (&sn)[1], f32x16& dpn, auto masked,
+                       auto has_next) __attribute__((always_inline)) {
+    if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
+    v8 ds[2];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * ps + e;
+        const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
+        ds[ps][e] = E::cvt(pr * (dp[i] - dl));
+      }
+    if constexpr (decltype(has_next)::value) products(j + 1, sn, dpn);
+    tr_product<E, D, FA_BWD_DQ_PIPE_FENCE>(kb[j % kBwdBufs], sz, ds, dq);
+  };
+  auto step = [&](int j, f32x16 (&s)[1], f32x16& dp, f32x16 (&sn)[1], f32x16& dpn)
+      __attribute__((always_inline)) {
+    copies(j + 2);  // past the end: empty ranges, nothing moves
+    if (j < wnt) {
+      if (j + 1 < wnt) {
+        if (j < wfull) iteration(j, s, dp, sn, dpn, std::false_type{}, std::true_type{});
+        else iteration(j, s, dp, sn, dpn, std::true_type{}, std::true_type{});
+      } else {
+        iteration(j, s, dp, sn, dpn, std::true_type{}, std::false_type{});
+      }
+    }
+    wait_vmem();  // tile j+2 landed: the next iteration reads tile j+2's products' operands
+    __syncthreads();
+  };
+  copies(0);
+  copies(1);
+  wait_vmem();
+  __syncthreads();
+  if (0 < wnt) products(0, sa, dpa);
+  for (int j = 0; j < nt; j += 2) {
+    step(j, sa, dpa, sb, dpb);
+    if (j + 1 < nt) step(j + 1, sb, dpb, sa, dpa);
+  }
+  if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
+}
+
 // MODE 0: dK and dV in one pass; 1: dV only; 2: dK only (S recomputed by both).
 template <class E, int D, bool CAUSAL, int MODE = 0>
 __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_dma(BwdParams p) {
@@ -3092,7 +3218,8 @@ hipError_t launch_backward_t(const BwdParams& p, hipStream_t stream) {
                                  dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
 #if FA_BWD_DMA
-  const void* kdq = (const void*)attn_bwd_dq_dma<E, D, C>;
+  const void* kdq = FA_BWD_DQ_PIPE ? (const void*)attn_bwd_dq_pipe<E, D, C>
+                                   : (const void*)attn_bwd_dq_dma<E, D, C>;
   const void* kkv = (const void*)attn_bwd_dkdv_dma<E, D, C>;
 #else
   const void* kdq = (const void*)attn_bwd_dq<E, D, C>;
