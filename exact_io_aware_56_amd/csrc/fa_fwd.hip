@@ -124,6 +124,9 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_PIPE_ORDER
 #define FA_PIPE_ORDER 0  // fenced stream: 0 every S product first, 1 S and P V alternating
 #endif
+#ifndef FA_PIPE_SKEW
+#define FA_PIPE_SKEW 0  // with FA_PIPE_NBUF=3: the second wave of each SIMD takes its barrier mid-tile
+#endif
 #ifndef FA_PIPE_NBUF
 #define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
 #endif
@@ -1676,13 +1679,21 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // end of iteration t only the copies of the last NB-2 iterations may still
   // be in flight. Copies past the end have an empty byte range and move
   // nothing, which keeps those counts exact.
-  constexpr int KEEP = (NB - 2) * (NDMA + NDMAV);
+  // Skewed barriers (three buffers): the second half of the waves (the
+  // second wave on each SIMD) takes its per-tile barrier between the two
+  // half-steps instead of after them, so the two waves sharing a SIMD run half
+  // a tile apart. Iteration t then refills the buffers of K t-1 (with K t+2)
+  // and V t-2 (with V t+1), which no wave of either group still reads, and
+  // each group waits for its own copies before its barrier.
+  constexpr bool SK = FA_PIPE_SKEW && !F8 && !WIN && !PF && NB == 3 && FA_PIPE_FENCE == 1;
+  constexpr int KEEP = SK ? 0 : (NB - 2) * (NDMA + NDMAV);
+  constexpr int KO = SK ? 2 : NB, VO = SK ? 1 : NB - 1;  // tiles ahead the copies fetch
   // fp8 V tiles take registers instead: loaded with the copies, stored to
   // vx just before the iteration's barrier.
   auto copies = [&](int t, unsigned char* kx, unsigned char* vx) __attribute__((always_inline)) {
-    copy_tile(t + NB, kx, std::false_type{});
-    if constexpr (F8) vload(t + NB - 1);
-    else copy_tile(t + NB - 1, vx, std::true_type{});
+    copy_tile(t + KO, kx, std::false_type{});
+    if constexpr (F8) vload(t + VO);
+    else copy_tile(t + VO, vx, std::true_type{});
   };
   auto sync_after = [&](unsigned char* vx) __attribute__((always_inline)) {
     if constexpr (F8) vstore(vx);
@@ -1690,7 +1701,11 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
     __syncthreads();
   };
 
-  if (!(PF && prefetched)) {
+  if constexpr (SK) {
+    copy_tile(0, k0s, std::false_type{});
+    copy_tile(1, k1s, std::false_type{});
+    copy_tile(0, v0s, std::true_type{});
+  } else if (!(PF && prefetched)) {
     copy_tile(0, k0s, std::false_type{});
 #pragma unroll
     for (int j = 1; j < NB; ++j) {
@@ -1734,7 +1749,48 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
       sync_after(vx);
     }
   }
-  for (; t + NB <= ts; t += NB) {
+  if constexpr (SK) {
+    const bool late = wave >= NW / 2;  // takes its barrier between the half-steps
+    auto half0 = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next, auto mask_a)
+        __attribute__((always_inline)) {
+      mma_half(kb, 0, sa, vb, pfa, has_next);
+      probs(sb, pfb, kbase + BC * t + 32, mask_a);
+    };
+    auto half1 = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next, auto mask_b)
+        __attribute__((always_inline)) {
+      mma_half(kb, 1, sb, vb, pfb, has_next);
+      if constexpr (decltype(has_next)::value) probs(sa, pfa, kbase + BC * (t + 1), mask_b);
+    };
+    // one tile: variant 0 unmasked with a next tile, 1 masked with a next
+    // tile, 2 the wave's last tile; every wave takes exactly one barrier
+    auto sk_step = [&](int t, int q, auto steady) __attribute__((always_inline)) {
+      unsigned char* kb = kbuf(q == 2 ? 0 : q + 1);
+      unsigned char* vb = vbuf(q);
+      unsigned char* vx = vbuf(q == 2 ? 0 : q + 1);
+      copies(t, kbuf(q == 0 ? 2 : q - 1), vx);
+      const bool live = decltype(steady)::value || t < rr.wnt;
+      const int var = decltype(steady)::value ? 0 : t + 1 < rr.wfull ? 0 : t + 1 < rr.wnt ? 1 : 2;
+      if (live) {
+        if (var == 0) half0(t, kb, vb, std::true_type{}, std::false_type{});
+        else if (var == 1) half0(t, kb, vb, std::true_type{}, std::true_type{});
+        else half0(t, kb, vb, std::false_type{}, std::true_type{});
+      }
+      if (late) sync_after(vx);
+      if (live) {
+        if (var == 0) half1(t, kb, vb, std::true_type{}, std::false_type{});
+        else if (var == 1) half1(t, kb, vb, std::true_type{}, std::true_type{});
+        else half1(t, kb, vb, std::false_type{}, std::false_type{});
+      }
+      if (!late) sync_after(vx);
+    };
+    for (; t + 3 <= ts; t += 3) {
+      static_for<3>([&](auto P) __attribute__((always_inline)) {
+        sk_step(t + decltype(P)::value, decltype(P)::value, std::true_type{});
+      });
+    }
+    for (; t < rr.nt; ++t) sk_step(t, t % 3, std::false_type{});
+  }
+  for (; t + NB <= ts && !SK; t += NB) {
     static_for<NB>([&](auto P) __attribute__((always_inline)) {
       constexpr int q = decltype(P)::value;
       copies(t + q, kbuf(q), vbuf((q + NB - 1) % NB));
@@ -1747,7 +1803,7 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // one among them), then the iterations in which only other waves of the
   // workgroup still compute. Masks are applied wherever a half may need one
   // (an unneeded mask changes nothing); three variants keep the code small.
-  for (; t < rr.nt; ++t) {
+  for (; t < rr.nt && !SK; ++t) {
     const int q = t % NB;
     unsigned char* kb = kbuf(q + 1 == NB ? 0 : q + 1);
     unsigned char* vb = vbuf(q);
