@@ -3227,9 +3227,12 @@ hipError_t launch_forward_varlen(Kind kind, int d, bool causal, const Params& p,
 }
 
 int decode_splits(int units_base, int Nk, int* chunk_tiles) {
-  // About 8 waves per CU in all, chunks of at least four 32-key tiles.
+  // About 4 waves per CU in all (one per SIMD), chunks of at least four
+  // 32-key tiles. Measured on the 16-sequence, 16K-key grouped decode: 1024
+  // waves 5.3 TB/s; 768 waves 4.8 (CUs left idle); 2048 waves 4.9, 4096 4.4
+  // (more concurrent key streams and partial results).
   const int nt = (Nk + 31) / 32;
-  const long long target = 2048;
+  const long long target = 1024;
   long long S = (target + units_base - 1) / units_base;
   S = std::max(1LL, std::min(S, (long long)(nt + 3) / 4));
   const int ct = (int)((nt + S - 1) / S);
