@@ -2309,6 +2309,9 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 #ifndef FA_BWD_DQ_PIPE_OCC
 #define FA_BWD_DQ_PIPE_OCC 1  // waves per SIMD it is compiled for (1: 512 registers)
 #endif
+#ifndef FA_BWD_XCD
+#define FA_BWD_XCD 1  // backward passes: XCD-aware order of the work units
+#endif
 #ifndef FA_BWD_FENCE_LA
 #define FA_BWD_FENCE_LA 1
 #endif
@@ -2318,6 +2321,19 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 #ifndef FA_BWD_WAVES
 #define FA_BWD_WAVES 4  // waves per workgroup of the backward passes
 #endif
+// The backward passes' work units in the order they are numbered (head by
+// head, longest first), dealt so that each XCD owns consecutive units: the
+// workgroups running together on an XCD then share their heads' tiles in its
+// L2, as in the forward kernels.
+__device__ __forceinline__ int bwd_block() {
+  int bid = blockIdx.x;
+  if constexpr (FA_BWD_XCD) {
+    const int total = gridDim.x;
+    if (total % kXcds == 0) bid = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+  }
+  return bid;
+}
+
 constexpr int kBwdWaves = FA_BWD_WAVES;    // waves per workgroup
 constexpr int kBwdRows = kBwdWaves * 32;   // query rows (dQ) or keys (dK/dV) per workgroup
 constexpr int kBwdSkew = 32;               // extra 16-bit elements per LDS row
@@ -2377,8 +2393,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = p.N;
-  const int bh = blockIdx.x / p.n_qt;
-  const int qt = p.n_qt - 1 - (blockIdx.x - bh * p.n_qt);  // longest causal tiles first
+  const int bid = bwd_block();
+  const int bh = bid / p.n_qt;
+  const int qt = p.n_qt - 1 - (bid - bh * p.n_qt);  // longest causal tiles first
   const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
   int kl = N;
   if (p.key_len != nullptr) {
@@ -2495,8 +2512,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dkdv(BwdParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = p.N;
-  const int kvh = blockIdx.x / p.n_kt;
-  const int kt = blockIdx.x - kvh * p.n_kt;
+  const int bid = bwd_block();
+  const int kvh = bid / p.n_kt;
+  const int kt = bid - kvh * p.n_kt;
   const int b = kvh / p.H_kv, g = kvh - b * p.H_kv;
   int kl = N;
   if (p.key_len != nullptr) {
@@ -2757,8 +2775,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = p.N;
-  const int bh = blockIdx.x / p.n_qt;
-  const int qt = p.n_qt - 1 - (blockIdx.x - bh * p.n_qt);
+  const int bid = bwd_block();
+  const int bh = bid / p.n_qt;
+  const int qt = p.n_qt - 1 - (bid - bh * p.n_qt);
   const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
   int kl = N;
   if (p.key_len != nullptr) {
@@ -2855,8 +2874,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_DQ_PIPE_OCC) void attn_bwd_d
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = p.N;
-  const int bh = blockIdx.x / p.n_qt;
-  const int qt = p.n_qt - 1 - (blockIdx.x - bh * p.n_qt);
+  const int bid = bwd_block();
+  const int bh = bid / p.n_qt;
+  const int qt = p.n_qt - 1 - (bid - bh * p.n_qt);
   const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
   int kl = N;
   if (p.key_len != nullptr) {
@@ -2969,8 +2989,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = p.N;
-  const int kvh = blockIdx.x / p.n_kt;
-  const int kt = blockIdx.x - kvh * p.n_kt;
+  const int bid = bwd_block();
+  const int kvh = bid / p.n_kt;
+  const int kt = bid - kvh * p.n_kt;
   const int b = kvh / p.H_kv, g = kvh - b * p.H_kv;
   int kl = N;
   if (p.key_len != nullptr) {
