@@ -8,8 +8,11 @@ N=8192, d=128, causal, 1% of the key rows scaled x8, scale 1/sqrt(128).
 
 Back-to-back launches of this kernel after an idle period run through the
 chip's power-management transient for a few dozen launches (per-launch times
-swing by up to 30% before they settle), so the default warm-up of 100 launches
-(about 50 ms) ends in the sustained state that the 200 timed launches measure.
+swing by up to 30% before they settle). Before the W warm-up steps the step is
+therefore launched back to back for --settle-ms of GPU time (200 ms by
+default, counted from the first launch's duration; reported as
+config.settle_launches), so that the timed steps measure the sustained state
+whatever W is.
 
 The K timed launches run back to back between two events on the launch
 stream; the p10 / median / p90 of single launches come from a further sample
@@ -39,6 +42,7 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak, bf16 causal B1 H32 N8192 d12
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp32": 157.3}
 EXP_PEAK_T = 256 * 4 * 8 * 2.4e9 / 1e12
 SPREAD_SAMPLE = 50  # steps timed one by one after the timed region
+SETTLE_CHUNK = 10  # steps per chunk of the settle phase
 KERNEL_SOURCES = ["exact_io_aware_56_amd/csrc/fa_fwd.hip", "exact_io_aware_56_amd/csrc/fa_api.cpp",
                   "exact_io_aware_56_amd/csrc/fa_internal.h"]
 
@@ -49,6 +53,40 @@ def kernel_sha() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def sq_counters(workload: str):
+    """MFMA busy fraction, VALU and LDS instructions per MFMA and the LDS bank
+    conflict rate of the kernel from the committed SQ counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_sq_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
+    if not sha or sha.group(1) != kernel_sha():
+        return None
+    out = {}
+    for key in ("mfma_busy_frac", "valu_per_mfma", "lds_per_mfma", "lds_bank_conflict_rate",
+                "valu_mfma_coexec_frac"):
+        m = re.search(key + r":\s*([0-9.eE+-]+)", text)
+        if m:
+            out[key] = float(m.group(1))
+    out["source"] = os.path.relpath(path, ROOT)
+    return out
+
+
+def host_cores() -> int:
+    """CPUs this process may run on."""
+    return len(os.sched_getaffinity(0))
+
+
+def blas_threads() -> int:
+    """Threads for the oracle's BLAS: this process's CPUs, capped by
+    OMP_NUM_THREADS when the environment sets it."""
+    n = host_cores()
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
 
 
 def measured_traffic(workload: str):
@@ -87,9 +125,16 @@ def algorithmic_bytes(spec, rows=None) -> int:
 def cpu_baseline_backward(w, budget_s: float):
     """The float64 backward oracle on whole heads until the budget is spent."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
 
+    threads = blas_threads()
+    with threadpool_limits(limits=threads):
+        return _cpu_baseline_backward(w, budget_s, threads, np, oracle)
+
+
+def _cpu_baseline_backward(w, budget_s, threads, np, oracle):
     s = w.spec
     q, k, v = w.exact()
     rng = np.random.default_rng(s.seed + 1)
@@ -109,32 +154,26 @@ def cpu_baseline_backward(w, budget_s: float):
             break
     dt = time.perf_counter() - t0
     flops = 2.5 * s.flops() / (s.B * s.H) * heads
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
-            "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": host_cores(),
+            "threads": threads, "kind": "oracle",
             "sample": f"{heads} of {s.B * s.H} heads of the same workload's backward, every "
                       f"query row, float64, {dt:.2f} s wall"}
 
 
-def _threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        return int(max([i["num_threads"] for i in threadpool_info()] or [1]))
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        return os.cpu_count() or 1
-
-
 def cpu_baseline(w, budget_s: float):
     """Time the float64 oracle on whole heads of the workload until the budget
-    is spent (at least one head); returns the JSON object."""
-    import numpy as np
+    is spent (at least one head), its BLAS on blas_threads() threads; returns
+    the JSON object."""
+    from threadpoolctl import threadpool_limits
 
+    threads = blas_threads()
+    with threadpool_limits(limits=threads):
+        return _cpu_baseline(w, budget_s, threads)
+
+
+def _cpu_baseline(w, budget_s: float, threads: int):
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i["num_threads"] for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = os.cpu_count() or 1
     s = w.spec
     q, k, v = w.exact()
     kl = w.key_len_or_none()
@@ -152,8 +191,8 @@ def cpu_baseline(w, budget_s: float):
             if time.perf_counter() - t0 >= budget_s:
                 break
         dt = time.perf_counter() - t0
-        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-                "kind": "oracle",
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": host_cores(),
+                "threads": threads, "kind": "oracle",
                 "sample": f"{done} of {s.B * s.H} (sequence, head) pairs of the same packed "
                           f"batch, every row, float64, {dt:.2f} s wall"}
     if s.is_decode:
@@ -167,7 +206,7 @@ def cpu_baseline(w, budget_s: float):
                 break
         dt = time.perf_counter() - t0
         return {"value": round(s.flops() / s.B * done / dt / 1e12, 6), "unit": "TFLOP/s",
-                "cores": int(threads), "kind": "oracle",
+                "cores": host_cores(), "threads": threads, "kind": "oracle",
                 "sample": f"{done} of {s.B} sequences of the same workload, every head, "
                           f"float64, {dt:.2f} s wall"}
     heads = 0
@@ -186,8 +225,8 @@ def cpu_baseline(w, budget_s: float):
             break
     dt = time.perf_counter() - t0
     flops = s.flops() / (s.B * s.H) * heads
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": host_cores(),
+            "threads": threads, "kind": "oracle",
             "sample": f"{heads} of {s.B * s.H} heads of the same workload, every query row, "
                       f"float64, {dt:.2f} s wall"}
 
@@ -204,6 +243,9 @@ def main(argv=None):
     ap.add_argument("--N", type=int, default=0,
                     help="override the workload's sequence length (HBM scaling runs); "
                          "such a line is not the headline measurement")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="GPU time of back-to-back steps run before the warm-up steps so that "
+                         "the chip's clocks settle (0 disables)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -283,15 +325,34 @@ def main(argv=None):
     def finite() -> bool:
         return bool(torch.isfinite(o.float()).all())
 
-    # The first warm-up launch is checked; the rest of the warm-up then runs
-    # straight into the timed launches with only the synchronisation between
-    # them, since any longer idle spell restarts the power-management transient.
-    if args.warmup > 0:
+    # The first launch is checked. Then the step runs back to back for at
+    # least --settle-ms of GPU time, in chunks whose events are read while the
+    # next chunk is already queued (so the GPU never idles), until the chip's
+    # clocks have left their power-management transient; then the W warm-up
+    # steps and the timed steps follow with only one synchronisation in
+    # between: any longer idle spell restarts the transient.
+    settle = 0
+    if args.warmup > 0 or args.settle_ms > 0:
         step()
         torch.cuda.synchronize()
         if not finite():
             print(json.dumps({"error": "non-finite output"}))
             return 4
+    if args.settle_ms > 0:
+        done_ms, prev = 0.0, None
+        while True:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(SETTLE_CHUNK):
+                step()
+            b.record(stream)
+            settle += SETTLE_CHUNK
+            if prev is not None:
+                prev[1].synchronize()
+                done_ms += prev[0].elapsed_time(prev[1])
+                if done_ms >= args.settle_ms or settle >= 20000:
+                    break
+            prev = (a, b)
 
     # The timed region is the K steps between two events on the launch stream,
     # with nothing else enqueued between the launches. The spread of single
@@ -302,7 +363,7 @@ def main(argv=None):
     n_spread = min(SPREAD_SAMPLE, args.steps)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
-    for _ in range(args.warmup - 1):
+    for _ in range(args.warmup - (1 if settle == 0 else 0)):
         step()
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
@@ -364,6 +425,7 @@ def main(argv=None):
                 "sequences": spec.B, "rows": int(w.q.shape[1]),
                 "lengths": "U{%d..%d}" % spec.key_len_range, "max_seqlen": spec.N},
             "outlier_keys_frac": spec.outlier_frac, "seed": spec.seed,
+            "settle_launches": settle,
             "spread_sample_steps": len(per),
             "launch_ms_p10": round(per[len(per) // 10], 5),
             "launch_ms_median": round(per[len(per) // 2], 5),
@@ -386,6 +448,9 @@ def main(argv=None):
                     "frac": round(exps / (avg_launch_ms * 1e-3) / 1e12 / EXP_PEAK_T, 4)},
         },
     }
+    counters = sq_counters(spec.name) if default_n and not args.backward else None
+    if counters is not None:
+        result["counters"] = counters
     if w.key_len is not None and (not spec.causal or spec.is_decode):
         eff = spec.flops() * float(w.key_len.sum()) / (spec.B * spec.N)
         result["config"]["effective_tflops"] = round(eff / (ms_per_step * 1e-3) / 1e12, 3)

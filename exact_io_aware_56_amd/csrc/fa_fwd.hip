@@ -79,13 +79,8 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #ifndef FA_WAVES_PER_EU
 #define FA_WAVES_PER_EU 2
 #endif
-#ifndef FA_16BIT_KERNEL
-// 16-bit inputs: 0 register-staged kernel, 1 direct-to-LDS kernel, 2 pipelined
-// kernel, 3 pipelined kernel for N >= FA_PIPE_MIN_N and direct-to-LDS below
-#define FA_16BIT_KERNEL 3
-#endif
 #ifndef FA_PIPE_MIN_N
-#define FA_PIPE_MIN_N 4096
+#define FA_PIPE_MIN_N 4096  // causal 16-bit sequences from this length take the pipelined kernel
 #endif
 #ifndef FA_DMA_WAVES
 #define FA_DMA_WAVES 4  // waves per workgroup of the direct-to-LDS kernel
@@ -98,43 +93,6 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #endif
 #ifndef FA_PIPE_IGLP
 #define FA_PIPE_IGLP 3  // pipelined kernel: the compiler's MFMA/exp interleave for each half-step (-1: none)
-#endif
-#ifndef FA_PIPE_PREFETCH
-#define FA_PIPE_PREFETCH 0  // pipelined kernel: next causal item's Q and first tiles under the epilogue
-#endif
-#ifndef FA_PIPE_FENCE
-// pipelined 16-bit kernel: S and P V products of a half-step as one operand
-// stream whose LDS reads are held FA_PIPE_LOOKAHEAD products ahead by
-// scheduling fences (0: the compiler places the reads; 2: the softmax of the
-// previous half is also placed by hand, one score per product)
-#define FA_PIPE_FENCE 1
-#endif
-#ifndef FA_DMA_FENCE
-#define FA_DMA_FENCE 1  // direct-to-LDS kernel: operand reads held FA_LOOKAHEAD products ahead by fences
-#endif
-#ifndef FA_WIN_PIPE
-#define FA_WIN_PIPE 0  // sliding windows on the pipelined kernel where it would take the unbanded case
-#endif
-#ifndef FA_D256_PIPE
-#define FA_D256_PIPE 1  // head dim 256 on the pipelined kernel (column slices) where d = 128 takes it
-#endif
-#ifndef FA_D256_FENCE
-#define FA_D256_FENCE 1  // head dim 256: operand reads held one product ahead by fences
-#endif
-#ifndef FA_PIPE_ORDER
-#define FA_PIPE_ORDER 0  // fenced stream: 0 every S product first, 1 S and P V alternating
-#endif
-#ifndef FA_PIPE_SKEW
-#define FA_PIPE_SKEW 0  // with FA_PIPE_NBUF=3: the second wave of each SIMD takes its barrier mid-tile
-#endif
-#ifndef FA_PIPE_NBUF
-#define FA_PIPE_NBUF 2  // LDS buffers per operand of the pipelined kernel (2 to 4)
-#endif
-#ifndef FA_WIDE_GROUPS
-#define FA_WIDE_GROUPS 1  // 32-row groups per wave of the pipelined kernel (1 or 2)
-#endif
-#ifndef FA_NBUF
-#define FA_NBUF 2  // LDS buffers per operand in the direct-to-LDS kernel (2 or 3)
 #endif
 #ifndef FA_LOOKAHEAD
 #define FA_LOOKAHEAD 2  // LDS operand reads issued this many MFMAs ahead
@@ -568,113 +526,6 @@ __device__ __forceinline__ void epilogue_staged(const Params& p, int bh, int row
 }
 
 // ---------------------------------------------------------------------------
-// bf16 / fp16 kernel
-// ---------------------------------------------------------------------------
-template <class E, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, FA_WAVES_PER_EU) void attn_fwd_16bit(Params p) {
-  using T = typename E::T;
-  using v8 = typename E::v8;
-  constexpr int BR = NW * 32;
-  constexpr int KS = D / 16;   // reduction steps over the head dim in S^T
-  constexpr int SB = BC / 32;  // 32-key blocks per tile
-  constexpr int DB = D / 32;   // 32-wide head-dim blocks of O^T
-  constexpr int KST = D + FA_K_SKEW;  // K row stride in LDS (elements)
-  constexpr int VST = D + FA_V_SKEW;  // V row stride in LDS (elements)
-  constexpr int NT = NW * 64;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  constexpr int CH = (BC * CPR + NT - 1) / NT;  // 16-byte chunks per thread per tile
-  constexpr bool kRagged = BC * CPR % NT != 0;  // the last chunk slot is idle on some threads
-
-  __shared__ __attribute__((aligned(16))) T ks[2][BC * KST];
-  __shared__ __attribute__((aligned(16))) T vs[2][BC * VST];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const RowRange rr = row_range<BR, BC, CAUSAL>(p, wave, l32);
-  const int N = p.N;
-  const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;
-  const T* Kh = (const T*)p.k + kv_head;
-  const T* Vh = (const T*)p.v + kv_head;
-
-  // Q^T operand: lane holds query row qrow, head-dim 16*s + 8*hi .. +7.
-  // Rows at or beyond N read as zeros.
-  v8 qf[KS];
-  {
-    const auto rq = tile_rsrc((const T*)p.q + head, rr.q_wg0 / BR, BR, N, D * (int)sizeof(T));
-    const int off = ((rr.qrow - rr.q_wg0) * D + 8 * hi) * (int)sizeof(T);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(v8, load16(rq, off + 32 * s));
-  }
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.0f;
-  const float thr = fminf(kRescaleLog2 / p.c, 1e30f);  // finite even for tiny scales
-
-  // Keys at or beyond key_len are loaded as zeros (so padded rows of V can
-  // never inject non-finite values through 0 * V); so is the tile past the
-  // last one, which the loop prefetches unconditionally.
-  const int kv_lim = rr.kl;
-  i32x4 kreg[CH], vreg[CH];
-  auto gload = [&](int j) __attribute__((always_inline)) {
-    const auto rk = tile_rsrc(Kh, j, BC, kv_lim, D * (int)sizeof(T));
-    const auto rv = tile_rsrc(Vh, j, BC, kv_lim, D * (int)sizeof(T));
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int chunk = tid + c * NT;
-      if (kRagged && chunk >= BC * CPR) continue;
-      const int off = ((chunk / CPR) * D + (chunk % CPR) * 8) * (int)sizeof(T);
-      kreg[c] = load16(rk, off);
-      vreg[c] = load16(rv, off);
-    }
-  };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int chunk = tid + c * NT;
-      const int r = chunk / CPR, col = (chunk % CPR) * 8;
-      if (kRagged && chunk >= BC * CPR) continue;
-      *(i32x4*)(&ks[buf][r * KST + col]) = kreg[c];
-      *(i32x4*)(&vs[buf][r * VST + col]) = vreg[c];
-    }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int j = 0; j < rr.nt; ++j) {
-    const int buf = j & 1;
-    gload(j + 1);
-    // The masked and unmasked tile bodies are separate code paths so the
-    // mask's selects are only paid on the boundary tiles.
-    auto tile = [&](auto masked) __attribute__((always_inline)) {
-      const T* kt = ks[buf];
-      f32x16 s[SB];
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        s[sb] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const v8 a = *(const v8*)(kt + (32 * sb + l32) * KST + 16 * st + 8 * hi);
-          s[sb] = E::mma(a, qf[st], s[sb]);
-        }
-      }
-      if constexpr (decltype(masked)::value) apply_mask<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi);
-      v8 pf[SB * 2];
-      online_softmax<E, SB, DB>(s, p.c, thr, m, l, o, pf);
-      pv_product<E, SB, DB, VST>(vs[buf], lane, pf, o);
-    };
-    if (j < rr.wfull) tile(std::false_type{});
-    else if (j < rr.wnt) tile(std::true_type{});
-    sstore(buf ^ 1);
-    __syncthreads();
-  }
-  epilogue<T, D, DB>(p, rr, hi, m, l, o);
-}
-
-// ---------------------------------------------------------------------------
 // Head dimension 256 (bf16 / fp16): each query tile is handled by two
 // workgroups, one per 128-column half of V and O. Both compute the whole S
 // (Q and K over all 256 dimensions, in the same order), so both arrive at the
@@ -767,7 +618,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_d256(Params p) {
     gload(j + 1);
     auto tile = [&](auto masked) __attribute__((always_inline)) {
       f32x16 sc[1] = {f32x16{}};
-      if constexpr (FA_D256_FENCE) {
+      {
         // operand reads held one product ahead (operand_fence)
         v8 ring[2];
 #pragma unroll
@@ -781,17 +632,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_d256(Params p) {
             operand_fence();
           }
         }
-      } else {
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const v8 a = *(const v8*)(ks[buf] + l32 * KST + 16 * st + 8 * hi);
-          sc[0] = E::mma(a, qf[st], sc[0]);
-        }
       }
       if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(sc, j * BC, rr.kl, rr.qrow, hi);
       v8 pf[2];
       online_softmax<E, 1, DB>(sc, p.c, thr, m, l, o, pf);
-      if constexpr (FA_D256_FENCE) {
+      {
         // O^T += V^T P^T as pv_product computes it, reads one product ahead
         const int row = 4 * hi + ((lane & 15) >> 2);
         const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -814,8 +659,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_d256(Params p) {
             operand_fence();
           }
         }
-      } else {
-        pv_product<E, 1, DB, VST>(vs[buf], lane, pf, o);
       }
     };
     if (j < rr.wfull) tile(std::false_type{});
@@ -903,21 +746,21 @@ __device__ __forceinline__ void wait_vmem_keep() {
 // bf16 / fp16 kernel (the default for 16-bit inputs)
 //
 // NW waves per workgroup (32 query rows each), two workgroups per CU at
-// NW = 4. K and V tiles reach LDS through the direct-to-LDS copies above,
-// NBUF buffers deep: the copy of tile j + NBUF - 1 lands while tile j is used.
-// Within a tile every MFMA's LDS operand is read kLookahead MFMAs ahead
-// through a small ring of registers, and the first V operands of O += P V are
-// read before the softmax arithmetic so that it hides their latency. The LDS
-// operand reads and their latency in front of each MFMA, not the arithmetic,
-// bound the register-staged kernel above; this one trims them.
+// NW = 4. K and V tiles reach LDS through the direct-to-LDS copies above, two
+// buffers deep: the copy of tile j + 1 lands while tile j is used. Within a
+// tile every MFMA's LDS operand is read FA_LOOKAHEAD MFMAs ahead through a
+// small ring of registers (held there by scheduling fences), and the first V
+// operands of O += P V are read before the softmax arithmetic so that it
+// hides their latency. Used for short causal sequences (the pipelined kernel
+// below takes the rest), sliding windows and packed batches of short
+// sequences.
 // ---------------------------------------------------------------------------
-template <class E, int D, int BC, int NW, int NBUF, bool CAUSAL, bool WIN = false, bool VL = false>
+template <class E, int D, int BC, int NW, bool CAUSAL, bool WIN = false, bool VL = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using v4 = typename E::v4;
   constexpr int BR = NW * 32;
-  static_assert(NBUF == 2 || NBUF == 3, "two or three LDS buffers per operand");
   constexpr int KS = D / 16;
   constexpr int SB = BC / 32;
   constexpr int DB = D / 32;
@@ -933,13 +776,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   // One named array per buffer (not one 2-D array): distinct objects let the
   // compiler see that an in-flight copy into one buffer cannot alias operand
   // reads from another, so it does not wait for the copy before them.
-  constexpr int TB3 = NBUF == 3 ? TB : 16;
   __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char k2s[TB3];
   __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v2s[TB3];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1038,19 +878,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
     for (int t = 0; t < NS + LA; ++t) {
       if (t < NS) {
         ring[t % (LA + 1)] = kfrag(kb, t);
-        if constexpr (FA_DMA_FENCE) operand_fence();
+        operand_fence();
       }
       const int u = t - LA;
       if (u >= 0) {
         s[u / KS] = E::mma(ring[u % (LA + 1)], qf[u % KS], s[u / KS]);
-        if constexpr (FA_DMA_FENCE) operand_fence();
+        operand_fence();
       }
     }
     // first V operands, in flight during the softmax
     v8 vring[LA + 1];
 #pragma unroll
     for (int t = 0; t < LA; ++t) vring[t] = vfrag(vb, t);
-    if constexpr (FA_DMA_FENCE) operand_fence();
+    operand_fence();
     if constexpr (decltype(masked)::value) {
       if constexpr (WIN)
         apply_mask_window<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi, p.win_left, p.win_right);
@@ -1064,23 +904,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
     for (int t = LA; t < NPV + LA; ++t) {
       if (t < NPV) {
         vring[t % (LA + 1)] = vfrag(vb, t);
-        if constexpr (FA_DMA_FENCE) operand_fence();
+        operand_fence();
       }
       const int u = t - LA;
       o[u % DB] = E::mma(vring[u % (LA + 1)], pf[u / DB], o[u % DB]);
-      if constexpr (FA_DMA_FENCE) operand_fence();
+      operand_fence();
     }
   };
-  // Iteration j uses buffer j % NBUF and copies tile j + NBUF - 1 into the
-  // buffer iteration j - 1 used. Copies are issued even for tiles past the end
-  // (their byte range is empty, so they move nothing) to keep the counts below
-  // exact: at the end of iteration j only the copies issued in it may remain
-  // in flight when NBUF == 3.
-  constexpr int KEEP = (NBUF - 2) * 2 * NDMA;  // copies one iteration may leave in flight
+  // Iteration j uses buffer j % 2 and copies tile j + 1 into the buffer
+  // iteration j - 1 used; every copy has landed at the end of an iteration.
+  // Copies past the last tile have an empty byte range and move nothing.
   auto step = [&](int j, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
                   unsigned char* vn) __attribute__((always_inline)) {
-    copy_tile(Kh, j + NBUF - 1, kn, std::false_type{});
-    copy_tile(Vh, j + NBUF - 1, vn, std::true_type{});
+    copy_tile(Kh, j + 1, kn, std::false_type{});
+    copy_tile(Vh, j + 1, vn, std::true_type{});
     if constexpr (WIN) {
       if (j >= wt0 && j < rr.wnt) {
         if (j >= whead && j < rr.wfull) tile(j, kc, vc, std::false_type{});
@@ -1090,30 +927,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
       if (j < rr.wfull) tile(j, kc, vc, std::false_type{});
       else if (j < rr.wnt) tile(j, kc, vc, std::true_type{});
     }
-    wait_vmem_keep<KEEP>();
+    wait_vmem();
     __syncthreads();
   };
 
   // Tiles are numbered from t0 (0 without a window); buffers follow j - t0.
   copy_tile(Kh, t0, k0s, std::false_type{});
   copy_tile(Vh, t0, v0s, std::true_type{});
-  if constexpr (NBUF == 3) {
-    copy_tile(Kh, t0 + 1, k1s, std::false_type{});
-    copy_tile(Vh, t0 + 1, v1s, std::true_type{});
-  }
-  wait_vmem_keep<KEEP>();
+  wait_vmem();
   __syncthreads();
-  if constexpr (NBUF == 2) {
-    for (int j = t0; j < rr.nt; j += 2) {
-      step(j, k0s, v0s, k1s, v1s);
-      if (j + 1 < rr.nt) step(j + 1, k1s, v1s, k0s, v0s);
-    }
-  } else {
-    for (int j = t0; j < rr.nt; j += 3) {
-      step(j, k0s, v0s, k2s, v2s);
-      if (j + 1 < rr.nt) step(j + 1, k1s, v1s, k0s, v0s);
-      if (j + 2 < rr.nt) step(j + 2, k2s, v2s, k1s, v1s);
-    }
+  for (int j = t0; j < rr.nt; j += 2) {
+    step(j, k0s, v0s, k1s, v1s);
+    if (j + 1 < rr.nt) step(j + 1, k1s, v1s, k0s, v0s);
   }
   epilogue<T, D, DB>(p, rr, hi, m, l, o);
 }
@@ -1149,10 +974,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // E::kPBound, which the 16-bit P and the fp32 accumulators hold without loss,
 // and O / l is the same exact softmax for any reference.
 //
-// With G = 2 a wave owns 64 query rows as two 32-row groups sharing every K
-// and V operand read; G = 1 keeps 32 rows per wave and two waves per SIMD.
-// Within a wave at most one key tile needs a mask (a tile covers a wave's row
-// range, see row_range), and it is the wave's last tile.
+// Each wave owns 32 query rows and two waves share each SIMD. Within a wave
+// at most one key tile needs a mask (a tile covers a wave's row range, see
+// row_range), and it is the wave's last tile.
 // ---------------------------------------------------------------------------
 
 // Bit cast between operand types of one size; a zero value otherwise (for
@@ -1167,22 +991,16 @@ __device__ __forceinline__ To same_size_cast(const From& x) {
 // and O, vh = 0 .. D/DV - 1, and computes the whole S over all D dimensions;
 // the workgroups of one query tile reach the same reference maxima and sums
 // with no communication, and the first one writes LSE.
-// WIN: banded mask (window) on top of the causal and padding masks.
-template <class E, int D, int G, int NW, int NB, bool CAUSAL, bool F8, bool VL = false, int DV = D,
-          bool WIN = false>
-__global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
+template <class E, int D, int NW, bool CAUSAL, bool F8, bool VL = false, int DV = D>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe(Params p) {
   using T = typename E::T;  // P, V in LDS and O (bfloat16 for fp8 inputs)
   using v8 = typename E::v8;
   using v4 = typename E::v4;
   using QT = std::conditional_t<F8, i32x8, v8>;  // one Q or K operand of the S product
-  static_assert(G == 1 || G == 2, "one or two 32-row groups per wave");
-  static_assert(!F8 || (G == 1 && NB == 2), "fp8 inputs: one row group, two buffers");
   static_assert(!(F8 && VL), "packed batches take 16-bit inputs");
-  static_assert(DV == D || (!F8 && !VL && G == 1 && D % DV == 0), "column slices: 16-bit, one row group");
-  static_assert(!WIN || (!F8 && !VL && DV == D), "windows: 16-bit inputs, whole rows");
+  static_assert(DV == D || (!F8 && !VL && D % DV == 0), "column slices: 16-bit inputs");
   constexpr int NVH = D / DV;  // workgroups per query tile (column slices of V and O)
-  constexpr int WR = 32 * G;   // query rows per wave
-  constexpr int BR = NW * WR;  // query rows per workgroup
+  constexpr int BR = NW * 32;  // query rows per workgroup
   constexpr int BC = 64;       // keys per LDS tile
   constexpr int KS = F8 ? D / 64 : D / 16;  // S MFMA steps over the head dim
   constexpr int DB = DV / 32;  // 32-wide blocks of the O^T columns this workgroup owns
@@ -1201,30 +1019,15 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   constexpr int LA = FA_PIPE_LOOKAHEAD;
   static_assert(F8 || NKC % NW == 0, "16-bit tiles must split into 1 KB copies per wave");
   static_assert(F8 || NVC % NW == 0, "16-bit V tiles must split into 1 KB copies per wave");
-  static_assert(NB >= 2 && NB <= 4, "two to four LDS buffers per operand");
 
   // One named array per buffer: distinct objects let the compiler see that a
   // copy in flight into one buffer cannot alias operand reads from another.
-  constexpr int TB2 = NB > 2 ? TB : 16, TB3 = NB > 3 ? TB : 16;
-  constexpr int TBV2 = NB > 2 ? TBV : 16, TBV3 = NB > 3 ? TBV : 16;
   __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char k2s[TB2];
-  __shared__ __attribute__((aligned(1024))) unsigned char k3s[TB3];
   __shared__ __attribute__((aligned(1024))) unsigned char v0s[TBV];
   __shared__ __attribute__((aligned(1024))) unsigned char v1s[TBV];
-  __shared__ __attribute__((aligned(1024))) unsigned char v2s[TBV2];
-  __shared__ __attribute__((aligned(1024))) unsigned char v3s[TBV3];
-  // With the cross-item prefetch the next item's first tiles land in the K/V
-  // buffers while this item's O is staged, so O gets a region of its own.
-  constexpr bool PF = FA_PIPE_PREFETCH && CAUSAL && !F8 && DV == D && !WIN;
-  __shared__ __attribute__((aligned(1024))) unsigned char ostage[PF ? NW * G * 32 * DV * 2 : 16];
-  auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* {
-    return i == 0 ? k0s : i == 1 ? k1s : i == 2 ? k2s : k3s;
-  };
-  auto vbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* {
-    return i == 0 ? v0s : i == 1 ? v1s : i == 2 ? v2s : v3s;
-  };
+  auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? k0s : k1s; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? v0s : v1s; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1265,30 +1068,24 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
 
   // Q^T operand: lane holds its query row's head-dim elements
   // [16*st + 8*hi, +8) (16-bit) or [64*st + 32*hi, +32) (fp8).
-  QT qf[G][KS];
+  QT qf[KS];
   auto load_q = [&](const RowRange& r) __attribute__((always_inline)) {
     const size_t qhead = (size_t)r.bh * N * D;
     const auto rq = tile_rsrc((const unsigned char*)p.q + qhead * (KRB / D), r.q_wg0 / BR, BR, N, KRB);
+    const int row = r.qrow - r.q_wg0;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int row = r.qrow + 32 * g - r.q_wg0;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if constexpr (F8) {
-          const int off = row * KRB + 64 * s + 32 * hi;
-          qf[g][s] = __builtin_shufflevector(load16(rq, off), load16(rq, off + 16), 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-          qf[g][s] = __builtin_bit_cast(v8, load16(rq, row * KRB + 32 * s + 16 * hi));
-        }
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (F8) {
+        const int off = row * KRB + 64 * s + 32 * hi;
+        qf[s] = __builtin_shufflevector(load16(rq, off), load16(rq, off + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        qf[s] = __builtin_bit_cast(v8, load16(rq, row * KRB + 32 * s + 16 * hi));
       }
     }
   };
 
-  // One query tile of one head, start to finish. With the prefetch, an item
-  // that follows another finds its Q and first K/V tiles already issued, and
-  // issues those of the item after it (nbh, nqt) before its own epilogue.
-  auto process = [&](int bh, int qt, bool prefetched, bool has_next, int nbh, int nqt)
-      __attribute__((always_inline)) {
+  // One query tile of one head, start to finish.
+  auto process = [&](int bh, int qt) __attribute__((always_inline)) {
   // Lane-derived offsets are recomputed per tile from an opaque copy of the
   // lane index, so that they are not kept live (and spilled) across tiles.
   const int ln = pinned_int(lane);
@@ -1315,66 +1112,21 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
       voff[db] = r * VRB + ((c ^ v_swz<DV>(r)) << 4) + 8 * (i & 1);
     }
   }
-  RowRange rr = row_range_at<BR, BC, CAUSAL, WR>(p, bh, qt, wave, l32);
-  // Sliding window: the workgroup streams key tiles from t0, the first tile
-  // any of its rows may see, counted from there: the K/V bases move t0 tiles
-  // on, so the tile indices, buffers and loop bounds below are relative to t0
-  // and kbase is the first key of tile 0. A wave's tiles before whead hold
-  // keys below the band of some of its rows and take the mask.
-  int kbase = 0, whead = 0;
-  if constexpr (WIN) {
-    const int wl = p.win_left, wr = p.win_right;
-    int t0 = 0;
-    if (wl >= 0) {
-      t0 = max(0, rr.q_wg0 - wl) / BC;
-      whead = (max(0, rr.qw0 + WR - 1 - wl) + BC - 1) / BC;
-    }
-    if (wr >= 0) {
-      rr.nt = min(rr.nt, (min(rr.kl, rr.q_wg0 + BR + wr) + BC - 1) / BC);
-      rr.wnt = min(rr.wnt, (max(0, min(rr.kl, rr.qw0 + WR + wr)) + BC - 1) / BC);
-      rr.wfull = min(rr.wfull, max(0, rr.qw0 + wr + 1) / BC);
-    }
-    t0 = __builtin_amdgcn_readfirstlane(t0);
-    kbase = t0 * BC;
-    rr.nt -= t0;
-    rr.wnt -= t0;
-    rr.wfull -= t0;
-    whead = __builtin_amdgcn_readfirstlane(whead - t0);
-  }
+  RowRange rr = row_range_at<BR, BC, CAUSAL>(p, bh, qt, wave, l32);
   const size_t head = (size_t)rr.bh * N * D, kv_head = (size_t)rr.kv_bh * N * D;  // elements
-  const unsigned char* Qh = (const unsigned char*)p.q + head * (KRB / D);
-  const unsigned char* Kh = (const unsigned char*)p.k + (kv_head + (size_t)kbase * D) * (KRB / D);
-  const unsigned char* Vh =
-      (const unsigned char*)p.v + (kv_head + (size_t)kbase * D) * (KRB / D) + vh * VRB;
-  const int kvl = WIN ? max(0, rr.kl - kbase) : rr.kl;  // valid key rows from tile 0 on
+  const unsigned char* Kh = (const unsigned char*)p.k + kv_head * (KRB / D);
+  const unsigned char* Vh = (const unsigned char*)p.v + kv_head * (KRB / D) + vh * VRB;
+  (void)head;
 
-  (void)Qh;
-  if (!(PF && prefetched)) load_q(rr);
+  load_q(rr);
   // One buffer resource per operand over the head's first kl key rows (the
   // host keeps a head under 1 GiB): a tile's copy only adds its byte offset,
   // and rows at or beyond kl (a ragged last tile, tiles past the end) read
   // as zeros.
-  const auto rsK = buffer_rsrc(Kh, kvl * KRB);
-  const auto rsV = buffer_rsrc(Vh, kvl * KRB);
+  const auto rsK = buffer_rsrc(Kh, rr.kl * KRB);
+  const auto rsV = buffer_rsrc(Vh, rr.kl * KRB);
   // K tile j (and V tile j for 16-bit inputs) straight into LDS, 16-byte
   // slots permuted per row as the operand reads expect.
-  auto copy_tile_with = [&](__amdgpu_buffer_rsrc_t rs, int j, unsigned char* dst, auto is_v)
-      __attribute__((always_inline)) {
-    constexpr bool IV = decltype(is_v)::value;
-    // rb: bytes per row in memory; an LDS row holds cpr 16-byte slots
-    constexpr int cpr = IV ? CPR : KCPR, rb = IV ? RB : KRB;
-    constexpr int nd = IV ? NDMAV : NDMA, nc = IV ? NVC : NKC;
-#pragma unroll
-    for (int c = 0; c < nd; ++c) {
-      const int blk = c * NW + wave;
-      if (nc % NW == 0 || blk < nc) {
-        const int slot = blk * 64 + lane;
-        const int r = slot / cpr, ps = slot % cpr;
-        const int lc = ps ^ (IV ? v_swz<DV>(r) : F8 ? k8_swz<D>(r) : k_swz<D>(r));
-        lds_copy16(rs, dst + blk * 1024, j * (BC * rb) + r * rb + (lc << 4));
-      }
-    }
-  };
   auto copy_tile = [&](int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
     constexpr bool IV = decltype(is_v)::value;
     // rb: bytes per row in memory; an LDS row holds cpr 16-byte slots
@@ -1430,112 +1182,80 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
         __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * VRB)));
     return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  // S^T = K Q^T over one 32-key half for every group, each K operand read once
-  auto scores = [&](const unsigned char* kb, int h, f32x16 (&s)[G]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = f32x16{};
+  // S^T = K Q^T over one 32-key half (the first tile, before the pipeline runs)
+  auto scores = [&](const unsigned char* kb, int h, f32x16& s) __attribute__((always_inline)) {
+    s = f32x16{};
     QT ring[LA + 1];
 #pragma unroll
     for (int t = 0; t < KS + LA; ++t) {
       if (t < KS) ring[t % (LA + 1)] = kfrag(kb, h, t);
       const int u = t - LA;
-      if (u >= 0)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if constexpr (F8)  // formats 0/0: fp8 e4m3 operands; E8M0 scales 127 = 1.0
-            s[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[u % (LA + 1)], qf[g][u], s[g],
-                                                                    0, 0, 0, 127, 0, 127);
-          else
-            s[g] = E::mma(ring[u % (LA + 1)], qf[g][u], s[g]);
-        }
+      if (u >= 0) {
+        if constexpr (F8)  // formats 0/0: fp8 e4m3 operands; E8M0 scales 127 = 1.0
+          s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[u % (LA + 1)], qf[u], s, 0, 0, 0,
+                                                              127, 0, 127);
+        else
+          s = E::mma(ring[u % (LA + 1)], qf[u], s);
+      }
     }
   };
 
-  f32x16 o[G][DB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[g][db] = f32x16{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   // m: reference maximum (raw score units); base = -m * c, +inf while m = -inf
-  float m[G], base[G], l[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) m[g] = -INFINITY, base[g] = INFINITY, l[g] = 0.0f;
+  float m = -INFINITY, base = INFINITY, l = 0.0f;
   const float c = p.c;
 
-  // O += V^T P^T over one 32-key half, each V operand read once
-  auto pv = [&](const unsigned char* vb, int h, const v8 (&pf)[G][2]) __attribute__((always_inline)) {
-    v8 ring[LA + 1];
-#pragma unroll
-    for (int t = 0; t < NPV + LA; ++t) {
-      if (t < NPV) ring[t % (LA + 1)] = vfrag(vb, h, t);
-      const int u = t - LA;
-      if (u >= 0)
-#pragma unroll
-        for (int g = 0; g < G; ++g) o[g][u % DB] = E::mma(ring[u % (LA + 1)], pf[g][u / DB], o[g][u % DB]);
-    }
-  };
-  // The masks of one half (its first key k0) for query row qrow.
-  auto mask_half = [&](f32x16& sh, int k0, int qrow) __attribute__((always_inline)) {
+  // The masks of one half (its first key k0) for this lane's query row.
+  auto mask_half = [&](f32x16& sh, int k0) __attribute__((always_inline)) {
     auto& s1 = *reinterpret_cast<f32x16(*)[1]>(&sh);
-    if constexpr (WIN) apply_mask_window<1, CAUSAL>(s1, k0, rr.kl, qrow, hi, p.win_left, p.win_right);
-    else apply_mask<1, CAUSAL>(s1, k0, rr.kl, qrow, hi);
+    apply_mask<1, CAUSAL>(s1, k0, rr.kl, rr.qrow, hi);
+  };
+  // The rare branch of probs: move the reference maximum of the rows of this
+  // half whose exponentials left the bound, rescale O and l, recompute P.
+  auto fix_probs = [&](const f32x16& s, v8 (&pf)[2], float& rs) __attribute__((always_inline)) {
+    float x = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) x = fmaxf(x, s[i]);
+    const float mn = fmaxf(m, max_halves(x));
+    const float alpha = pinned(mn == m ? 1.0f : fast_exp2((m - mn) * c));
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    m = mn;
+    base = -mn * c;
+    const float bu = mn == -INFINITY ? 0.0f : base;
+    rs = 0.0f;
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[ps][e] = E::cvt(fast_exp2(fmaf(s[8 * ps + e], c, bu)));
+      rs = E::sum8(pf[ps], rs);
+    }
   };
   // P of one half from its raw scores s (k0 = its first key); updates l and,
-  // on the rare branch, m, base and O.
-  // The rare branch of probs: move the reference maxima of the rows of this
-  // half whose exponentials left the bound, rescale O and l, recompute P.
-  auto fix_probs = [&](f32x16 (&s)[G], v8 (&pf)[G][2], float (&rs)[G]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float x = s[g][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) x = fmaxf(x, s[g][i]);
-      const float mn = fmaxf(m[g], max_halves(x));
-      const float alpha = pinned(mn == m[g] ? 1.0f : fast_exp2((m[g] - mn) * c));
-      l[g] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha;
-      m[g] = mn;
-      base[g] = -mn * c;
-      const float bu = mn == -INFINITY ? 0.0f : base[g];
-      rs[g] = 0.0f;
-#pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[g][ps][e] = E::cvt(fast_exp2(fmaf(s[g][8 * ps + e], c, bu)));
-        rs[g] = E::sum8(pf[g][ps], rs[g]);
-      }
-    }
-  };
-  auto probs = [&](f32x16 (&s)[G], v8 (&pf)[G][2], int k0, auto masked) __attribute__((always_inline)) {
-    float rs[G];
-    bool bad = false;
+  // on the rare branch, m, base and O. The running sum adds the same rounded
+  // P values that multiply V, so the weights applied to V's rows sum to one up
+  // to fp32 accumulation.
+  auto probs = [&](f32x16& s, v8 (&pf)[2], int k0, auto masked) __attribute__((always_inline)) {
     if constexpr (FA_PIPE_IGLP >= 0) __builtin_amdgcn_iglp_opt(FA_PIPE_IGLP);
+    if constexpr (decltype(masked)::value) mask_half(s, k0);
+    float rs = 0.0f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if constexpr (decltype(masked)::value)
-        mask_half(s[g], k0, rr.qrow + 32 * g);
-      rs[g] = 0.0f;
+    for (int ps = 0; ps < 2; ++ps) {
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[g][ps][e] = E::cvt(fast_exp2(fmaf(s[g][8 * ps + e], c, base[g])));
-        rs[g] = E::sum8(pf[g][ps], rs[g]);
-      }
-      bad |= !(rs[g] <= E::kPBound);
+      for (int e = 0; e < 8; ++e) pf[ps][e] = E::cvt(fast_exp2(fmaf(s[8 * ps + e], c, base)));
+      rs = E::sum8(pf[ps], rs);
     }
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) fix_probs(s, pf, rs);
-#pragma unroll
-    for (int g = 0; g < G; ++g) l[g] += rs[g];
+    if (__builtin_amdgcn_ballot_w64(!(rs <= E::kPBound)) != 0) fix_probs(s, pf, rs);
+    l += rs;
   };
 
-  f32x16 sa[G], sb[G];
-  v8 pfa[G][2], pfb[G][2];
-  // One iteration: tile t's V (vb) and tile t+1's K (kb). On entry sb holds
-  // S of half 2t+1 and pfa P of half 2t; on exit sb holds S of half 2t+3 and
-  // pfa P of half 2t+2.
+  f32x16 sa, sb;
+  v8 pfa[2], pfb[2];
   // The S product of half h of the K tile at kb (when hn) and O += V^T P^T of
   // half h of the V tile at vb as one stream of products: each operand read
   // is issued LA products before the product that takes it, and fences that
@@ -1544,270 +1264,113 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // leave every product waiting out a whole LDS latency). The softmax
   // arithmetic that follows in program order still moves up among them.
   constexpr int kFence = 0x2 | 0x4 | 0x10 | 0x400;  // VALU, SALU, VMEM, transcendental
-  auto mma_half = [&](const unsigned char* kb, int h, f32x16 (&s)[G], const unsigned char* vb,
-                      const v8 (&pf)[G][2], auto hn) __attribute__((always_inline)) {
+  auto mma_half = [&](const unsigned char* kb, int h, f32x16& s, const unsigned char* vb,
+                      const v8 (&pf)[2], auto hn) __attribute__((always_inline)) {
     constexpr int NS = decltype(hn)::value ? KS : 0;
     constexpr int NT = NS + NPV;
-    if constexpr (NS > 0)
-#pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = f32x16{};
-    // stream position t -> S step (is_s) or P V step, and its index
-    constexpr bool ALT = FA_PIPE_ORDER == 1 && NS == NPV;
-    auto is_s = [](int t) { return ALT ? t % 2 == 0 : t < NS; };
-    auto idx = [](int t) { return ALT ? t / 2 : t < NS ? t : t - NS; };
+    if constexpr (NS > 0) s = f32x16{};
     v8 ring[LA + 1];
-#pragma unroll
-    for (int t = 0; t < NT + LA; ++t) {
-      if (t < NT) {
-        if (is_s(t)) ring[t % (LA + 1)] = same_size_cast<v8>(kfrag(kb, h, idx(t)));
-        else ring[t % (LA + 1)] = vfrag(vb, h, idx(t));
-        __builtin_amdgcn_sched_barrier(kFence);
-      }
-      const int u = t - LA;
-      if (u >= 0) {
-        const int i = idx(u);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (is_s(u)) s[g] = E::mma(ring[u % (LA + 1)], same_size_cast<v8>(qf[g][i]), s[g]);
-          else o[g][i % DB] = E::mma(ring[u % (LA + 1)], pf[g][i / DB], o[g][i % DB]);
-        }
-        __builtin_amdgcn_sched_barrier(kFence);
-      }
-    }
-  };
-  // mma_half with the softmax of another half (raw scores s_in -> P pf_out)
-  // spread evenly under its products in program order, nothing allowed to
-  // move across: each product slot takes its share of the scores' FMA and
-  // exponential, and the conversion and row sum of the pair finished one
-  // slot earlier. Ends with the bound check of probs.
-  auto unit = [&](const unsigned char* kb, int h, f32x16 (&s)[G], const unsigned char* vb,
-                  const v8 (&pf)[G][2], f32x16 (&s_in)[G], v8 (&pf_out)[G][2], int k0, auto hn,
-                  auto masked, auto dp) __attribute__((always_inline)) {
-    constexpr bool DP = decltype(dp)::value;
-    constexpr int NS = decltype(hn)::value ? KS : 0;
-    constexpr int NT = NS + NPV;
-    constexpr int SPS = 16 / NT;  // scores per product slot
-    static_assert(16 % NT == 0, "whole scores per slot");
-    constexpr int kHard = 0x4 | 0x10;  // only scalar and global-memory instructions cross
-    float rs[G], e[G][16];
-    if constexpr (DP) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if constexpr (decltype(masked)::value)
-          mask_half(s_in[g], k0, rr.qrow + 32 * g);
-        rs[g] = 0.0f;
-      }
-    }
-    auto pair_done = [&](int i) __attribute__((always_inline)) {  // scores i, i+1 -> P, row sum
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        pf_out[g][i / 8][i % 8] = E::cvt(e[g][i]);
-        pf_out[g][i / 8][i % 8 + 1] = E::cvt(e[g][i + 1]);
-        rs[g] = E::sum2(pf_out[g][i / 8][i % 8], pf_out[g][i / 8][i % 8 + 1], rs[g]);
-      }
-    };
-    if constexpr (NS > 0)
-#pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = f32x16{};
-    v8 ring[LA + 1];
-    __builtin_amdgcn_sched_barrier(kHard);
 #pragma unroll
     for (int t = 0; t < NT + LA; ++t) {
       if (t < NT) {
         if (t < NS) ring[t % (LA + 1)] = same_size_cast<v8>(kfrag(kb, h, t));
         else ring[t % (LA + 1)] = vfrag(vb, h, t - NS);
-        __builtin_amdgcn_sched_barrier(kHard);
+        __builtin_amdgcn_sched_barrier(kFence);
       }
       const int u = t - LA;
       if (u >= 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (u < NS) s[g] = E::mma(ring[u % (LA + 1)], same_size_cast<v8>(qf[g][u]), s[g]);
-          else o[g][(u - NS) % DB] = E::mma(ring[u % (LA + 1)], pf[g][(u - NS) / DB], o[g][(u - NS) % DB]);
-        }
-        __builtin_amdgcn_sched_barrier(kHard);
-        if constexpr (DP) {
-#pragma unroll
-          for (int k = 0; k < SPS; ++k) {
-            const int i = u * SPS + k;
-#pragma unroll
-            for (int g = 0; g < G; ++g) e[g][i] = fast_exp2(fmaf(s_in[g][i], c, base[g]));
-          }
-          // the pairs whose second exponential was issued a slot earlier
-#pragma unroll
-          for (int i = 0; i < 16; i += 2)
-            if (i + 1 >= (u - 1) * SPS && i + 1 < u * SPS) pair_done(i);
-          __builtin_amdgcn_sched_barrier(kHard);
-        }
+        if (u < NS) s = E::mma(ring[u % (LA + 1)], same_size_cast<v8>(qf[u]), s);
+        else o[(u - NS) % DB] = E::mma(ring[u % (LA + 1)], pf[(u - NS) / DB], o[(u - NS) % DB]);
+        __builtin_amdgcn_sched_barrier(kFence);
       }
     }
-    if constexpr (DP) {
+  };
+  // For fp8 inputs: the S product of half h (scaled fp8 MFMAs, K operands read
+  // just ahead) and then O += V^T P^T of half h in bf16.
+  auto mma_half_f8 = [&](const unsigned char* kb, int h, f32x16& s, const unsigned char* vb,
+                         const v8 (&pf)[2], auto hn) __attribute__((always_inline)) {
+    if constexpr (decltype(hn)::value) scores(kb, h, s);
+    v8 ring[LA + 1];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2)
-        if (i + 1 >= (NT - 1) * SPS) pair_done(i);
-      bool bad = false;
-#pragma unroll
-      for (int g = 0; g < G; ++g) bad |= !(rs[g] <= E::kPBound);
-      if (__builtin_amdgcn_ballot_w64(bad) != 0) fix_probs(s_in, pf_out, rs);
-#pragma unroll
-      for (int g = 0; g < G; ++g) l[g] += rs[g];
+    for (int t = 0; t < NPV + LA; ++t) {
+      if (t < NPV) ring[t % (LA + 1)] = vfrag(vb, h, t);
+      const int u = t - LA;
+      if (u >= 0) o[u % DB] = E::mma(ring[u % (LA + 1)], pf[u / DB], o[u % DB]);
     }
   };
+  // One iteration: tile t's V (vb) and tile t+1's K (kb). On entry sb holds
+  // S of half 2t+1 and pfa P of half 2t; on exit sb holds S of half 2t+3 and
+  // pfa P of half 2t+2.
   auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next,
                        auto mask_a, auto mask_b) __attribute__((always_inline)) {
-    if constexpr (FA_PIPE_FENCE == 2 && !F8) {
-      unit(kb, 0, sa, vb, pfa, sb, pfb, kbase + BC * t + 32, has_next, mask_a, std::true_type{});
-      unit(kb, 1, sb, vb, pfb, sa, pfa, kbase + BC * (t + 1), has_next, mask_b, has_next);
-      return;
-    }
-    if constexpr (FA_PIPE_FENCE && !F8) {
-      mma_half(kb, 0, sa, vb, pfa, has_next);
-      probs(sb, pfb, kbase + BC * t + 32, mask_a);
-      mma_half(kb, 1, sb, vb, pfb, has_next);
+    if constexpr (F8) {
+      mma_half_f8(kb, 0, sa, vb, pfa, has_next);
+      probs(sb, pfb, BC * t + 32, mask_a);
+      mma_half_f8(kb, 1, sb, vb, pfb, has_next);
     } else {
-      if constexpr (decltype(has_next)::value) scores(kb, 0, sa);
-      pv(vb, 0, pfa);
-      probs(sb, pfb, kbase + BC * t + 32, mask_a);
-      if constexpr (decltype(has_next)::value) scores(kb, 1, sb);
-      pv(vb, 1, pfb);
+      mma_half(kb, 0, sa, vb, pfa, has_next);
+      probs(sb, pfb, BC * t + 32, mask_a);
+      mma_half(kb, 1, sb, vb, pfb, has_next);
     }
-    if constexpr (decltype(has_next)::value) probs(sa, pfa, kbase + BC * (t + 1), mask_b);
+    if constexpr (decltype(has_next)::value) probs(sa, pfa, BC * (t + 1), mask_b);
   };
-  // K tile j lives in buffer j % NB, V tile j in buffer j % NB. Iteration t
-  // reads K t+1 and V t and refills the buffers of K t (with K t+NB) and of
-  // V t-1 (with V t+NB-1), so every copy has NB-1 iterations to land; at the
-  // end of iteration t only the copies of the last NB-2 iterations may still
-  // be in flight. Copies past the end have an empty byte range and move
-  // nothing, which keeps those counts exact.
-  // Skewed barriers (three buffers): the second half of the waves (the
-  // second wave on each SIMD) takes its per-tile barrier between the two
-  // half-steps instead of after them, so the two waves sharing a SIMD run half
-  // a tile apart. Iteration t then refills the buffers of K t-1 (with K t+2)
-  // and V t-2 (with V t+1), which no wave of either group still reads, and
-  // each group waits for its own copies before its barrier.
-  constexpr bool SK = FA_PIPE_SKEW && !F8 && !WIN && !PF && NB == 3 && FA_PIPE_FENCE == 1;
-  constexpr int KEEP = SK ? 0 : (NB - 2) * (NDMA + NDMAV);
-  constexpr int KO = SK ? 2 : NB, VO = SK ? 1 : NB - 1;  // tiles ahead the copies fetch
+  // K tile j lives in buffer j % 2, V tile j in buffer j % 2. Iteration t
+  // reads K t+1 and V t and refills the buffers of K t (with K t+2) and of
+  // V t-1 (with V t+1), so every copy has a whole iteration to land; at the
+  // end of an iteration every copy has landed. Copies past the end have an
+  // empty byte range and move nothing.
   // fp8 V tiles take registers instead: loaded with the copies, stored to
   // vx just before the iteration's barrier.
   auto copies = [&](int t, unsigned char* kx, unsigned char* vx) __attribute__((always_inline)) {
-    copy_tile(t + KO, kx, std::false_type{});
-    if constexpr (F8) vload(t + VO);
-    else copy_tile(t + VO, vx, std::true_type{});
+    copy_tile(t + 2, kx, std::false_type{});
+    if constexpr (F8) vload(t + 1);
+    else copy_tile(t + 1, vx, std::true_type{});
   };
   auto sync_after = [&](unsigned char* vx) __attribute__((always_inline)) {
     if constexpr (F8) vstore(vx);
-    wait_vmem_keep<KEEP>();
+    wait_vmem();
     __syncthreads();
   };
 
-  if constexpr (SK) {
-    copy_tile(0, k0s, std::false_type{});
-    copy_tile(1, k1s, std::false_type{});
+  copy_tile(0, k0s, std::false_type{});
+  copy_tile(1, k1s, std::false_type{});
+  if constexpr (F8) {
+    vload(0);
+    vstore(v0s);
+  } else {
     copy_tile(0, v0s, std::true_type{});
-  } else if (!(PF && prefetched)) {
-    copy_tile(0, k0s, std::false_type{});
-#pragma unroll
-    for (int j = 1; j < NB; ++j) {
-      copy_tile(j, kbuf(j), std::false_type{});
-      if constexpr (F8) {
-        vload(j - 1);
-        vstore(vbuf(j - 1));
-      } else {
-        copy_tile(j - 1, vbuf(j - 1), std::true_type{});
-      }
-    }
   }
-  wait_vmem_keep<KEEP>();
+  wait_vmem();
   __syncthreads();
   if (rr.wnt > 0) {
     scores(k0s, 0, sa);
     scores(k0s, 1, sb);
-    if (0 < rr.wfull && (!WIN || 0 >= whead)) probs(sa, pfa, kbase, std::false_type{});
-    else probs(sa, pfa, kbase, std::true_type{});
+    if (0 < rr.wfull) probs(sa, pfa, 0, std::false_type{});
+    else probs(sa, pfa, 0, std::true_type{});
   }
   __syncthreads();  // K of tile 0 is read by every wave before its buffer is refilled
-  // Iterations [0, ts): every half unmasked and a next tile to score; NB of
+  // Iterations [0, ts): every half unmasked and a next tile to score; two of
   // them per pass so that every buffer is named at compile time.
   const int ts = max(0, rr.wfull - 1);
   int t = 0;
-  if constexpr (WIN) {
-    // The wave's masked head, in whole passes of NB iterations so that the
-    // steady loop starts on buffer 0 (every wave still takes one barrier per
-    // tile, whatever its head's length).
-    const int hs = min(rr.nt, (max(0, whead) + NB - 1) / NB * NB);
-    for (; t < hs; ++t) {
-      const int q = t % NB;
-      unsigned char* kb = kbuf(q + 1 == NB ? 0 : q + 1);
-      unsigned char* vb = vbuf(q);
-      unsigned char* vx = vbuf(q == 0 ? NB - 1 : q - 1);
-      copies(t, kbuf(q), vx);
-      if (t < rr.wnt) {
-        if (t + 1 < rr.wnt) iteration(t, kb, vb, std::true_type{}, std::true_type{}, std::true_type{});
-        else iteration(t, kb, vb, std::false_type{}, std::true_type{}, std::false_type{});
-      }
-      sync_after(vx);
-    }
-  }
-  if constexpr (SK) {
-    const bool late = wave >= NW / 2;  // takes its barrier between the half-steps
-    auto half0 = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next, auto mask_a)
-        __attribute__((always_inline)) {
-      mma_half(kb, 0, sa, vb, pfa, has_next);
-      probs(sb, pfb, kbase + BC * t + 32, mask_a);
-    };
-    auto half1 = [&](int t, const unsigned char* kb, const unsigned char* vb, auto has_next, auto mask_b)
-        __attribute__((always_inline)) {
-      mma_half(kb, 1, sb, vb, pfb, has_next);
-      if constexpr (decltype(has_next)::value) probs(sa, pfa, kbase + BC * (t + 1), mask_b);
-    };
-    // one tile: variant 0 unmasked with a next tile, 1 masked with a next
-    // tile, 2 the wave's last tile; every wave takes exactly one barrier
-    auto sk_step = [&](int t, int q, auto steady) __attribute__((always_inline)) {
-      unsigned char* kb = kbuf(q == 2 ? 0 : q + 1);
-      unsigned char* vb = vbuf(q);
-      unsigned char* vx = vbuf(q == 2 ? 0 : q + 1);
-      copies(t, kbuf(q == 0 ? 2 : q - 1), vx);
-      const bool live = decltype(steady)::value || t < rr.wnt;
-      const int var = decltype(steady)::value ? 0 : t + 1 < rr.wfull ? 0 : t + 1 < rr.wnt ? 1 : 2;
-      if (live) {
-        if (var == 0) half0(t, kb, vb, std::true_type{}, std::false_type{});
-        else if (var == 1) half0(t, kb, vb, std::true_type{}, std::true_type{});
-        else half0(t, kb, vb, std::false_type{}, std::true_type{});
-      }
-      if (late) sync_after(vx);
-      if (live) {
-        if (var == 0) half1(t, kb, vb, std::true_type{}, std::false_type{});
-        else if (var == 1) half1(t, kb, vb, std::true_type{}, std::true_type{});
-        else half1(t, kb, vb, std::false_type{}, std::false_type{});
-      }
-      if (!late) sync_after(vx);
-    };
-    for (; t + 3 <= ts; t += 3) {
-      static_for<3>([&](auto P) __attribute__((always_inline)) {
-        sk_step(t + decltype(P)::value, decltype(P)::value, std::true_type{});
-      });
-    }
-    for (; t < rr.nt; ++t) sk_step(t, t % 3, std::false_type{});
-  }
-  for (; t + NB <= ts && !SK; t += NB) {
-    static_for<NB>([&](auto P) __attribute__((always_inline)) {
+  for (; t + 2 <= ts; t += 2) {
+    static_for<2>([&](auto P) __attribute__((always_inline)) {
       constexpr int q = decltype(P)::value;
-      copies(t + q, kbuf(q), vbuf((q + NB - 1) % NB));
-      iteration(t + q, kbuf((q + 1) % NB), vbuf(q), std::true_type{}, std::false_type{},
+      copies(t + q, kbuf(q), vbuf(q ^ 1));
+      iteration(t + q, kbuf(q ^ 1), vbuf(q), std::true_type{}, std::false_type{},
                 std::false_type{});
-      sync_after(vbuf((q + NB - 1) % NB));
+      sync_after(vbuf(q ^ 1));
     });
   }
   // The rest: the last steady iterations, the wave's last tiles (the masked
   // one among them), then the iterations in which only other waves of the
   // workgroup still compute. Masks are applied wherever a half may need one
   // (an unneeded mask changes nothing); three variants keep the code small.
-  for (; t < rr.nt && !SK; ++t) {
-    const int q = t % NB;
-    unsigned char* kb = kbuf(q + 1 == NB ? 0 : q + 1);
+  for (; t < rr.nt; ++t) {
+    const int q = t & 1;
+    unsigned char* kb = kbuf(q ^ 1);
     unsigned char* vb = vbuf(q);
-    unsigned char* vx = vbuf(q == 0 ? NB - 1 : q - 1);
+    unsigned char* vx = vbuf(q ^ 1);
     copies(t, kbuf(q), vx);
     if (t < rr.wnt) {
       if (t + 1 < rr.wfull) iteration(t, kb, vb, std::true_type{}, std::false_type{}, std::false_type{});
@@ -1820,42 +1383,16 @@ __global__ __launch_bounds__(NW * 64, 3 - G) void attn_fwd_pipe(Params p) {
   // now stage O (8 KB per wave for D = 128, two waves per buffer).
   wait_vmem();
   __syncthreads();
-  if constexpr (PF) {
-    if (has_next) {
-      // The next item's Q and first tiles, issued now that every wave is done
-      // with the K/V buffers; they land while this item's O is written.
-      const RowRange rn = row_range_at<BR, BC, CAUSAL, WR>(p, nbh, nqt, wave, l32);
-      load_q(rn);
-      const size_t nkv = (size_t)rn.kv_bh * N * D;
-      const auto nK = buffer_rsrc((const unsigned char*)p.k + nkv * (KRB / D), rn.kl * KRB);
-      const auto nV = buffer_rsrc((const unsigned char*)p.v + nkv * (KRB / D), rn.kl * KRB);
-      copy_tile_with(nK, 0, k0s, std::false_type{});
-#pragma unroll
-      for (int j = 1; j < NB; ++j) {
-        copy_tile_with(nK, j, kbuf(j), std::false_type{});
-        copy_tile_with(nV, j - 1, vbuf(j - 1), std::true_type{});
-      }
-    }
-  }
-  static_assert(NW * G <= 8 && TB >= 2 * 32 * DV * 2 && TBV >= 2 * 32 * DV * 2, "O staging space");
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int slot = wave * G + g;
-    unsigned char* stage = PF ? ostage + slot * (32 * DV * 2)
-                              : (slot < 2 ? k0s : slot < 4 ? k1s : slot < 6 ? v0s : v1s) +
-                                    (slot & 1) * (32 * DV * 2);
-    epilogue_staged<T, DV, DB, D>(p, rr.bh, rr.qw0 + 32 * g, lane, m[g], l[g], o[g], stage, vh * DV,
-                                  vh == 0);
-  }
-  // staging reads done before the next tile's copies land (a region of its
-  // own with the prefetch: each wave only ever reuses its own slice)
-  if constexpr (!PF) __syncthreads();
+  static_assert(NW <= 8 && TB >= 2 * 32 * DV * 2 && TBV >= 2 * 32 * DV * 2, "O staging space");
+  unsigned char* stage = (wave < 2 ? k0s : wave < 4 ? k1s : wave < 6 ? v0s : v1s) + (wave & 1) * (32 * DV * 2);
+  epilogue_staged<T, DV, DB, D>(p, rr.bh, rr.qw0, lane, m, l, o, stage, vh * DV, vh == 0);
+  // staging reads done before the next tile's copies land
+  __syncthreads();
   };
 
   const int items = CAUSAL && u != n_qt - 1 - u ? 2 : 1;
 #pragma nounroll
-  for (int it = 0; it < items; ++it)
-    process(bh, CAUSAL && it == 0 ? n_qt - 1 - u : u, it > 0, it + 1 < items, bh, u);
+  for (int it = 0; it < items; ++it) process(bh, CAUSAL && it == 0 ? n_qt - 1 - u : u);
 }
 
 // ---------------------------------------------------------------------------
@@ -2273,47 +1810,17 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),  Delta = rowsum(dO * O),
 //   dQ = scale * dS K,  dK = scale * dS^T Q,  P = exp2(c*s - LSE*log2(e)).
 // Three passes on one stream: attn_bwd_prep writes Delta and LSE*log2(e) per
-// query row; attn_bwd_dq gives every wave 32 query rows and streams the
+// query row; attn_bwd_dq_dma gives every wave 32 query rows and streams the
 // 32-key K/V tiles (the forward's orientation: lanes own queries, so LSE and
-// Delta are per-lane values); attn_bwd_dkdv gives every wave 32 keys and
+// Delta are per-lane values); attn_bwd_dkdv_dma gives every wave 32 keys and
 // streams 32-query Q/dO tiles over the query heads that share its K/V head
 // (lanes own keys, so dK and dV accumulate with no cross-wave reduction and
 // no atomics). Both recompute S; products whose second operand comes out of
-// an accumulator (dQ from dS^T, dV from P, dK from dS) use pv_product, the
-// forward's transposing-read product.
+// an accumulator (dQ from dS^T, dV from P, dK from dS) read that tile with
+// the forward's transposing LDS reads (tr_product).
 // ---------------------------------------------------------------------------
-#ifndef FA_BWD_DMA
-#define FA_BWD_DMA 1  // backward passes on direct-to-LDS copies (0: register-staged tiles)
-#endif
-#ifndef FA_BWD_SPLIT
-#define FA_BWD_SPLIT 0  // 1: dV and dK in separate passes (each recomputes S)
-#endif
 #ifndef FA_BWD_KV_OCC
 #define FA_BWD_KV_OCC 2  // waves per SIMD the dK/dV pass is compiled for (1: 512 registers)
-#endif
-#ifndef FA_BWD_FENCE
-// dK/dV pass: operand reads held ahead of their products by scheduling
-// fences, FA_BWD_FENCE_LA products ahead (0: the compiler places the reads,
-// FA_BWD_LOOKAHEAD ahead in program order)
-#define FA_BWD_FENCE 0
-#endif
-#ifndef FA_BWD_DQ_FENCE
-#define FA_BWD_DQ_FENCE 0  // the same fences for the dQ pass alone (FA_BWD_FENCE: the dK/dV pass)
-#endif
-#ifndef FA_BWD_DQ_PIPE
-#define FA_BWD_DQ_PIPE 0  // dQ pass with the next key tile's products under this tile's dS work
-#endif
-#ifndef FA_BWD_DQ_PIPE_FENCE
-#define FA_BWD_DQ_PIPE_FENCE 1  // its operand reads held one product ahead by fences
-#endif
-#ifndef FA_BWD_DQ_PIPE_OCC
-#define FA_BWD_DQ_PIPE_OCC 1  // waves per SIMD it is compiled for (1: 512 registers)
-#endif
-#ifndef FA_BWD_XCD
-#define FA_BWD_XCD 1  // backward passes: XCD-aware order of the work units
-#endif
-#ifndef FA_BWD_FENCE_LA
-#define FA_BWD_FENCE_LA 1
 #endif
 #ifndef FA_BWD_LOOKAHEAD
 #define FA_BWD_LOOKAHEAD 2  // backward passes: LDS operand reads issued this many MFMAs ahead
@@ -2326,17 +1833,12 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 // workgroups running together on an XCD then share their heads' tiles in its
 // L2, as in the forward kernels.
 __device__ __forceinline__ int bwd_block() {
-  int bid = blockIdx.x;
-  if constexpr (FA_BWD_XCD) {
-    const int total = gridDim.x;
-    if (total % kXcds == 0) bid = (bid % kXcds) * (total / kXcds) + bid / kXcds;
-  }
-  return bid;
+  const int bid = blockIdx.x, total = gridDim.x;
+  return total % kXcds == 0 ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
 }
 
 constexpr int kBwdWaves = FA_BWD_WAVES;    // waves per workgroup
 constexpr int kBwdRows = kBwdWaves * 32;   // query rows (dQ) or keys (dK/dV) per workgroup
-constexpr int kBwdSkew = 32;               // extra 16-bit elements per LDS row
 
 // Delta and LSE * log2(e) of every query row: D/8 lanes per row, 16 bytes each.
 template <class T, int D>
@@ -2378,266 +1880,10 @@ __device__ __forceinline__ void store_grad(T* row_ptr, int hi, float scale, cons
     }
 }
 
-template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq(BwdParams p) {
-  using T = typename E::T;
-  using v8 = typename E::v8;
-  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, ST = D + kBwdSkew;
-  constexpr int NT = kBwdWaves * 64;
-  constexpr int CH = (32 * CPR + NT - 1) / NT;  // 16-byte pieces per thread per tile
-  constexpr bool kRagged = 32 * CPR % NT != 0;  // some threads idle on the last piece
-  __shared__ __attribute__((aligned(16))) T ks[2][32 * ST];
-  __shared__ __attribute__((aligned(16))) T vs[2][32 * ST];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int N = p.N;
-  const int bid = bwd_block();
-  const int bh = bid / p.n_qt;
-  const int qt = p.n_qt - 1 - (bid - bh * p.n_qt);  // longest causal tiles first
-  const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
-  int kl = N;
-  if (p.key_len != nullptr) {
-    const int x = p.key_len[b];
-    kl = x < 0 ? 0 : (x > N ? N : x);
-  }
-  kl = __builtin_amdgcn_readfirstlane(kl);
-  const int q_wg0 = qt * kBwdRows, qw0 = q_wg0 + 32 * wave, qrow = qw0 + l32;
-  int kv_end = kl;
-  if (CAUSAL) kv_end = min(kv_end, min(N, q_wg0 + kBwdRows));
-  const int nt = (kv_end + 31) / 32;
-  int w_end = CAUSAL ? min(kv_end, qw0 + 32) : kv_end;
-  if (qw0 >= N) w_end = 0;
-  const int wnt = (w_end + 31) / 32;
-  int wfull = kl / 32;
-  if (CAUSAL) wfull = min(wfull, (qw0 + 1) / 32);
-  wfull = min(wfull, wnt);
-
-  const size_t head = (size_t)bh * N * D, kv_head = (size_t)kvh * N * D;
-  const T* Kh = (const T*)p.k + kv_head;
-  const T* Vh = (const T*)p.v + kv_head;
-  v8 qf[KS], df[KS];
-  {
-    const auto rq = tile_rsrc((const T*)p.q + head, 0, N, N, D * 2);
-    const auto rd = tile_rsrc((const T*)p.dout + head, 0, N, N, D * 2);
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      qf[st] = __builtin_bit_cast(v8, load16(rq, qrow * D * 2 + 32 * st + 16 * hi));
-      df[st] = __builtin_bit_cast(v8, load16(rd, qrow * D * 2 + 32 * st + 16 * hi));
-    }
-  }
-  const bool row_ok = qrow < N;
-  const float lse2 = row_ok ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
-  const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.0f;
-  const float c = p.c;
-
-  i32x4 kreg[CH], vreg[CH];
-  auto gload = [&](int j) __attribute__((always_inline)) {
-    const auto rk = tile_rsrc(Kh, j, 32, kv_end, D * 2);
-    const auto rv = tile_rsrc(Vh, j, 32, kv_end, D * 2);
-#pragma unroll
-    for (int cc = 0; cc < CH; ++cc) {
-      const int piece = tid + cc * NT;
-      if (kRagged && piece >= 32 * CPR) continue;
-      const int off = ((piece / CPR) * D + (piece % CPR) * 8) * 2;
-      kreg[cc] = load16(rk, off);
-      vreg[cc] = load16(rv, off);
-    }
-  };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int cc = 0; cc < CH; ++cc) {
-      const int piece = tid + cc * NT;
-      if (kRagged && piece >= 32 * CPR) continue;
-      const int r = piece / CPR, col = (piece % CPR) * 8;
-      *(i32x4*)(&ks[buf][r * ST + col]) = kreg[cc];
-      *(i32x4*)(&vs[buf][r * ST + col]) = vreg[cc];
-    }
-  };
-
-  f32x16 dq[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    const int buf = j & 1;
-    gload(j + 1);
-    auto tile = [&](auto masked) __attribute__((always_inline)) {
-      f32x16 s[1] = {f32x16{}};
-      f32x16 dp = {};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const v8 a = *(const v8*)(ks[buf] + l32 * ST + 16 * st + 8 * hi);
-        s[0] = E::mma(a, qf[st], s[0]);
-        const v8 bv = *(const v8*)(vs[buf] + l32 * ST + 16 * st + 8 * hi);
-        dp = E::mma(bv, df[st], dp);
-      }
-      if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
-      v8 ds[2];
-#pragma unroll
-      for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * ps + e;
-          const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
-          ds[ps][e] = E::cvt(pr * (dp[i] - dl));
-        }
-      pv_product<E, 1, DB, ST>(ks[buf], lane, ds, dq);
-    };
-    if (j < wfull) tile(std::false_type{});
-    else if (j < wnt) tile(std::true_type{});
-    sstore(buf ^ 1);
-    __syncthreads();
-  }
-  if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
-}
-
-template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dkdv(BwdParams p) {
-  using T = typename E::T;
-  using v8 = typename E::v8;
-  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, ST = D + kBwdSkew;
-  constexpr int NT = kBwdWaves * 64;
-  constexpr int CH = (32 * CPR + NT - 1) / NT;
-  constexpr bool kRagged = 32 * CPR % NT != 0;
-  __shared__ __attribute__((aligned(16))) T qs[2][32 * ST];
-  __shared__ __attribute__((aligned(16))) T dos[2][32 * ST];
-  __shared__ __attribute__((aligned(16))) float ls[2][32];
-  __shared__ __attribute__((aligned(16))) float dls[2][32];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int N = p.N;
-  const int bid = bwd_block();
-  const int kvh = bid / p.n_kt;
-  const int kt = bid - kvh * p.n_kt;
-  const int b = kvh / p.H_kv, g = kvh - b * p.H_kv;
-  int kl = N;
-  if (p.key_len != nullptr) {
-    const int x = p.key_len[b];
-    kl = x < 0 ? 0 : (x > N ? N : x);
-  }
-  kl = __builtin_amdgcn_readfirstlane(kl);
-  const int k_wg0 = kt * kBwdRows, kw0 = k_wg0 + 32 * wave, key = kw0 + l32;
-  // Query tiles [t_begin, nqt) of every query head in the group; none if the
-  // workgroup's keys are all padding.
-  const int nqt = (N + 31) / 32;
-  const int t_begin = CAUSAL ? k_wg0 / 32 : 0;
-  const int per_head = k_wg0 < kl ? nqt - t_begin : 0;
-  const int n_iter = per_head * p.group;
-  const bool wave_live = kw0 < kl;
-
-  const size_t kv_head = (size_t)kvh * N * D;
-  v8 kf[KS], vf[KS];
-  {
-    const auto rk = tile_rsrc((const T*)p.k + kv_head, 0, N, N, D * 2);
-    const auto rv = tile_rsrc((const T*)p.v + kv_head, 0, N, N, D * 2);
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      kf[st] = __builtin_bit_cast(v8, load16(rk, key * D * 2 + 32 * st + 16 * hi));
-      vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
-    }
-  }
-  const float c = p.c;
-
-  i32x4 qreg[CH], dreg[CH];
-  float lreg = INFINITY, dlreg = 0.0f;
-  auto gload = [&](int u) __attribute__((always_inline)) {
-    const int hq = g * p.group + (per_head > 0 ? u / max(per_head, 1) : 0);
-    const int t = t_begin + (per_head > 0 ? u % max(per_head, 1) : 0);
-    const size_t qhead = ((size_t)b * p.H + hq) * N;
-    const bool any = u < n_iter;
-    const auto rq = tile_rsrc((const T*)p.q + qhead * D, t, 32, any ? N : 0, D * 2);
-    const auto rd = tile_rsrc((const T*)p.dout + qhead * D, t, 32, any ? N : 0, D * 2);
-#pragma unroll
-    for (int cc = 0; cc < CH; ++cc) {
-      const int piece = tid + cc * NT;
-      if (kRagged && piece >= 32 * CPR) continue;
-      const int off = ((piece / CPR) * D + (piece % CPR) * 8) * 2;
-      qreg[cc] = load16(rq, off);
-      dreg[cc] = load16(rd, off);
-    }
-    if (tid < 32) {
-      const int row = 32 * t + tid;
-      const bool ok = any && row < N;
-      lreg = ok ? p.lse2[qhead + row] : INFINITY;
-      dlreg = ok ? p.delta[qhead + row] : 0.0f;
-    }
-  };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int cc = 0; cc < CH; ++cc) {
-      const int piece = tid + cc * NT;
-      if (kRagged && piece >= 32 * CPR) continue;
-      const int r = piece / CPR, col = (piece % CPR) * 8;
-      *(i32x4*)(&qs[buf][r * ST + col]) = qreg[cc];
-      *(i32x4*)(&dos[buf][r * ST + col]) = dreg[cc];
-    }
-    if (tid < 32) {
-      ls[buf][tid] = lreg;
-      dls[buf][tid] = dlreg;
-    }
-  };
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dk[db] = f32x16{}, dv[db] = f32x16{};
-  if (n_iter > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int u = 0; u < n_iter; ++u) {
-    const int buf = u & 1;
-    const int t = t_begin + u % per_head;
-    gload(u + 1);
-    // this wave's keys see some query of the tile
-    if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const v8 a = *(const v8*)(qs[buf] + l32 * ST + 16 * st + 8 * hi);
-        s = E::mma(a, kf[st], s);
-        const v8 d = *(const v8*)(dos[buf] + l32 * ST + 16 * st + 8 * hi);
-        dp = E::mma(d, vf[st], dp);
-      }
-      // element i is query 32t + r(i), r(i) = 8*(i/4) + 4*hi + i%4, key `key`
-      v8 pf[2], dsf[2];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = *(const f32x4*)(&ls[buf][8 * q4 + 4 * hi]);
-        const f32x4 d4 = *(const f32x4*)(&dls[buf][8 * q4 + 4 * hi]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * q4 + e;
-          const int qry = 32 * t + 8 * q4 + 4 * hi + e;
-          const bool ok = key < kl && (!CAUSAL || key <= qry);
-          const float pr = ok ? fast_exp2(fmaf(s[i], c, -l4[e])) : 0.0f;
-          pf[i >> 3][i & 7] = E::cvt(pr);
-          dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
-        }
-      }
-      pv_product<E, 1, DB, ST>(dos[buf], lane, pf, dv);
-      pv_product<E, 1, DB, ST>(qs[buf], lane, dsf, dk);
-    }
-    sstore(buf ^ 1);
-    __syncthreads();
-  }
-  if (key < N) {
-    store_grad<T, DB>((T*)p.dk + kv_head + (size_t)key * D, hi, p.scale, dk);
-    store_grad<T, DB>((T*)p.dv + kv_head + (size_t)key * D, hi, 1.0f, dv);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Backward passes on direct-to-LDS copies: the same arithmetic as attn_bwd_dq /
-// attn_bwd_dkdv, but the streamed 32-row tiles reach LDS through
-// buffer_load ... lds (no staging registers), three buffers deep, so a tile's
-// copy is issued two iterations before it is used. Every tile is stored with
+// The streamed 32-row tiles of both passes reach LDS through buffer_load ...
+// lds (no staging registers), three buffers deep, so a tile's copy is issued
+// two iterations before it is used. Every tile is stored with
 // the V-operand slot permutation (v_swz): transposing reads use it as the
 // forward's V reads do, and row reads (the A operands of S and dP) look their
 // 16-byte slot up through the same permutation.
@@ -2665,18 +1911,14 @@ struct SwzTile {
   __device__ __forceinline__ int row(int c) const { return roff + ((c ^ sw) << 4); }
 };
 
-// FN: operand reads held ahead of their products by fences (operand_fence).
-template <bool FN>
-constexpr int bwd_la() { return FN ? FA_BWD_FENCE_LA : FA_BWD_LOOKAHEAD; }
-
 // acc^T[n][col] += sum_k Y[k][n] * M[k][col] over the 32 rows k of a swizzled
 // tile Y, M given as the packed 16-bit operand of a D-layout accumulator.
-template <class E, int D, bool FN>
+template <class E, int D>
 __device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzTile<D>& sz,
                                            const typename E::v8 (&m)[2], f32x16 (&acc)[D / 32]) {
   using v4 = typename E::v4;
   using v8 = typename E::v8;
-  constexpr int DB = D / 32, RB = D * 2, LA = bwd_la<FN>();
+  constexpr int DB = D / 32, RB = D * 2, LA = FA_BWD_LOOKAHEAD;
   v8 ring[LA + 1];
 #pragma unroll
   for (int t = 0; t < 2 * DB + LA; ++t) {
@@ -2686,61 +1928,34 @@ __device__ __forceinline__ void tr_product(const unsigned char* tile, const SwzT
       const v4 a1 = __builtin_bit_cast(
           v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + 8 * RB)));
       ring[t % (LA + 1)] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-      if constexpr (FN) operand_fence();
     }
     const int u = t - LA;
-    if (u >= 0) {
-      acc[u % DB] = E::mma(ring[u % (LA + 1)], m[u / DB], acc[u % DB]);
-      if constexpr (FN) operand_fence();
-    }
-  }
-}
-
-// S = X Y^T alone (as two_products without the second product).
-template <class E, int D, bool FN>
-__device__ __forceinline__ void one_product(const unsigned char* x, const SwzTile<D>& sz, int hi,
-                                            const typename E::v8 (&y)[D / 16], f32x16& s) {
-  using v8 = typename E::v8;
-  constexpr int KS = D / 16, LA = bwd_la<FN>();
-  v8 ra[LA + 1];
-#pragma unroll
-  for (int t = 0; t < KS + LA; ++t) {
-    if (t < KS) {
-      ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
-      if constexpr (FN) operand_fence();
-    }
-    const int u = t - LA;
-    if (u >= 0) {
-      s = E::mma(ra[u % (LA + 1)], y[u], s);
-      if constexpr (FN) operand_fence();
-    }
+    if (u >= 0) acc[u % DB] = E::mma(ring[u % (LA + 1)], m[u / DB], acc[u % DB]);
   }
 }
 
 // S = X Y^T and dP = Z W^T over the head dim for one 32-row tile: X, Z rows
 // of swizzled LDS tiles (A operands), Y, W in registers (B operands); operand
 // reads issued FA_BWD_LOOKAHEAD steps ahead.
-template <class E, int D, bool FN>
+template <class E, int D>
 __device__ __forceinline__ void two_products(const unsigned char* x, const unsigned char* z,
                                              const SwzTile<D>& sz, int hi,
                                              const typename E::v8 (&y)[D / 16],
                                              const typename E::v8 (&w)[D / 16], f32x16& s,
                                              f32x16& dp) {
   using v8 = typename E::v8;
-  constexpr int KS = D / 16, LA = bwd_la<FN>();
+  constexpr int KS = D / 16, LA = FA_BWD_LOOKAHEAD;
   v8 ra[LA + 1], rb[LA + 1];
 #pragma unroll
   for (int t = 0; t < KS + LA; ++t) {
     if (t < KS) {
       ra[t % (LA + 1)] = *(const v8*)(x + sz.row(2 * t + hi));
       rb[t % (LA + 1)] = *(const v8*)(z + sz.row(2 * t + hi));
-      if constexpr (FN) operand_fence();
     }
     const int u = t - LA;
     if (u >= 0) {
       s = E::mma(ra[u % (LA + 1)], y[u], s);
       dp = E::mma(rb[u % (LA + 1)], w[u], dp);
-      if constexpr (FN) operand_fence();
     }
   }
 }
@@ -2833,7 +2048,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
     auto tile = [&](auto masked) __attribute__((always_inline)) {
       f32x16 s[1] = {f32x16{}};
       f32x16 dp = {};
-      two_products<E, D, FA_BWD_DQ_FENCE>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
+      two_products<E, D>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
       if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
       v8 ds[2];
 #pragma unroll
@@ -2844,7 +2059,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
           const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
           ds[ps][e] = E::cvt(pr * (dp[i] - dl));
         }
-      tr_product<E, D, FA_BWD_DQ_FENCE>(kb[buf], sz, ds, dq);
+      tr_product<E, D>(kb[buf], sz, ds, dq);
     };
     if (j < wfull) tile(std::false_type{});
     else if (j < wnt) tile(std::true_type{});
@@ -2855,126 +2070,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
 }
 
-// The dQ pass with the forward's cross-tile overlap: in iteration j the S and
-// dP products of key tile j+1 are issued among the vector instructions that
-// turn tile j's S and dP into dS, and dQ += dS K of tile j follows. Tiles j
-// and j+1 are resident (three buffers; the copy of tile j+2 goes into the
-// buffer of tile j-1) and each copy lands within the iteration it is issued
-// in. Two register sets for S and dP alternate between even and odd tiles.
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_DQ_PIPE_OCC) void attn_bwd_dq_pipe(BwdParams p) {
-  using T = typename E::T;
-  using v8 = typename E::v8;
-  constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
-  __shared__ __attribute__((aligned(1024))) unsigned char kb[kBwdBufs][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char vb[kBwdBufs][TB];
-  static_assert(kBwdBufs == 3, "tiles j and j+1 resident while tile j+2 is copied");
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int N = p.N;
-  const int bid = bwd_block();
-  const int bh = bid / p.n_qt;
-  const int qt = p.n_qt - 1 - (bid - bh * p.n_qt);
-  const int b = bh / p.H, kvh = b * p.H_kv + (bh - b * p.H) / p.group;
-  int kl = N;
-  if (p.key_len != nullptr) {
-    const int x = p.key_len[b];
-    kl = x < 0 ? 0 : (x > N ? N : x);
-  }
-  kl = __builtin_amdgcn_readfirstlane(kl);
-  const int q_wg0 = qt * kBwdRows, qw0 = q_wg0 + 32 * wave, qrow = qw0 + l32;
-  int kv_end = kl;
-  if (CAUSAL) kv_end = min(kv_end, min(N, q_wg0 + kBwdRows));
-  const int nt = (kv_end + 31) / 32;
-  int w_end = CAUSAL ? min(kv_end, qw0 + 32) : kv_end;
-  if (qw0 >= N) w_end = 0;
-  const int wnt = (w_end + 31) / 32;
-  int wfull = kl / 32;
-  if (CAUSAL) wfull = min(wfull, (qw0 + 1) / 32);
-  wfull = min(wfull, wnt);
-
-  const size_t head = (size_t)bh * N * D, kv_head = (size_t)kvh * N * D;
-  const T* Kh = (const T*)p.k + kv_head;
-  const T* Vh = (const T*)p.v + kv_head;
-  v8 qf[KS], df[KS];
-  {
-    const auto rq = tile_rsrc((const T*)p.q + head, 0, N, N, D * 2);
-    const auto rd = tile_rsrc((const T*)p.dout + head, 0, N, N, D * 2);
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      qf[st] = __builtin_bit_cast(v8, load16(rq, qrow * D * 2 + 32 * st + 16 * hi));
-      df[st] = __builtin_bit_cast(v8, load16(rd, qrow * D * 2 + 32 * st + 16 * hi));
-    }
-  }
-  const bool row_ok = qrow < N;
-  const float lse2 = row_ok ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
-  const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.0f;
-  const float c = p.c;
-  SwzTile<D> sz;
-  sz.init(pinned_int(lane));
-
-  auto copies = [&](int j) __attribute__((always_inline)) {
-    const int buf = j % kBwdBufs;
-    copy_rows_swz<D>(Kh, j, kv_end, kb[buf], wave, lane);
-    copy_rows_swz<D>(Vh, j, kv_end, vb[buf], wave, lane);
-  };
-  f32x16 dq[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
-  f32x16 sa[1], dpa, sb[1], dpb;
-  // S and dP of tile j into (s, dp)
-  auto products = [&](int j, f32x16 (&s)[1], f32x16& dp) __attribute__((always_inline)) {
-    s[0] = f32x16{};
-    dp = f32x16{};
-    two_products<E, D, FA_BWD_DQ_PIPE_FENCE>(kb[j % kBwdBufs], vb[j % kBwdBufs], sz, hi, qf, df, s[0], dp);
-  };
-  // dS of tile j from its S and dP (masked when the tile needs it), then
-  // the next tile's products (when it has one) and dQ += dS K of tile j.
-  auto iteration = [&](int j, f32x16 (&s)[1], f32x16& dp, f32x16 (&sn)[1], f32x16& dpn, auto masked,
-                       auto has_next) __attribute__((always_inline)) {
-    if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
-    v8 ds[2];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 8 * ps + e;
-        const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
-        ds[ps][e] = E::cvt(pr * (dp[i] - dl));
-      }
-    if constexpr (decltype(has_next)::value) products(j + 1, sn, dpn);
-    tr_product<E, D, FA_BWD_DQ_PIPE_FENCE>(kb[j % kBwdBufs], sz, ds, dq);
-  };
-  auto step = [&](int j, f32x16 (&s)[1], f32x16& dp, f32x16 (&sn)[1], f32x16& dpn)
-      __attribute__((always_inline)) {
-    copies(j + 2);  // past the end: empty ranges, nothing moves
-    if (j < wnt) {
-      if (j + 1 < wnt) {
-        if (j < wfull) iteration(j, s, dp, sn, dpn, std::false_type{}, std::true_type{});
-        else iteration(j, s, dp, sn, dpn, std::true_type{}, std::true_type{});
-      } else {
-        iteration(j, s, dp, sn, dpn, std::true_type{}, std::false_type{});
-      }
-    }
-    wait_vmem();  // tile j+2 landed: the next iteration reads tile j+2's products' operands
-    __syncthreads();
-  };
-  copies(0);
-  copies(1);
-  wait_vmem();
-  __syncthreads();
-  if (0 < wnt) products(0, sa, dpa);
-  for (int j = 0; j < nt; j += 2) {
-    step(j, sa, dpa, sb, dpb);
-    if (j + 1 < nt) step(j + 1, sb, dpb, sa, dpa);
-  }
-  if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
-}
-
-// MODE 0: dK and dV in one pass; 1: dV only; 2: dK only (S recomputed by both).
-template <class E, int D, bool CAUSAL, int MODE = 0>
 __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_dma(BwdParams p) {
   using T = typename E::T;
   using v8 = typename E::v8;
@@ -3014,7 +2110,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       kf[st] = __builtin_bit_cast(v8, load16(rk, key * D * 2 + 32 * st + 16 * hi));
-      if constexpr (MODE != 1) vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
+      vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
     }
   }
   const float c = p.c;
@@ -3069,8 +2165,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     copies(u + 2, (u + 2) % kBwdBufs);
     if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
       f32x16 s = {}, dp = {};
-      if constexpr (MODE == 1) one_product<E, D, FA_BWD_FENCE>(qb[buf], sz, hi, kf, s);
-      else two_products<E, D, FA_BWD_FENCE>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
+      two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
       v8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -3083,11 +2178,11 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
           const bool ok = key < kl && (!CAUSAL || key <= qry);
           const float pr = ok ? fast_exp2(fmaf(s[i], c, -l4[e])) : 0.0f;
           pf[i >> 3][i & 7] = E::cvt(pr);
-          if constexpr (MODE != 1) dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
+          dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
         }
       }
-      if constexpr (MODE != 2) tr_product<E, D, FA_BWD_FENCE>(ob[buf], sz, pf, dv);
-      if constexpr (MODE != 1) tr_product<E, D, FA_BWD_FENCE>(qb[buf], sz, dsf, dk);
+      tr_product<E, D>(ob[buf], sz, pf, dv);
+      tr_product<E, D>(qb[buf], sz, dsf, dk);
     }
     wait_vmem_keep<2 * NCPW>();  // row stats u+1 and tile u+1 landed; tile u+2 may be in flight
     if (tid < 32) ls[nbuf][tid] = lreg, dls[nbuf][tid] = dlreg;
@@ -3095,8 +2190,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   }
   wait_vmem();
   if (key < N) {
-    if constexpr (MODE != 1) store_grad<T, DB>((T*)p.dk + kv_head + (size_t)key * D, hi, p.scale, dk);
-    if constexpr (MODE != 2) store_grad<T, DB>((T*)p.dv + kv_head + (size_t)key * D, hi, 1.0f, dv);
+    store_grad<T, DB>((T*)p.dk + kv_head + (size_t)key * D, hi, p.scale, dk);
+    store_grad<T, DB>((T*)p.dv + kv_head + (size_t)key * D, hi, 1.0f, dv);
   }
 }
 
@@ -3121,33 +2216,21 @@ hipError_t launch(K kernel, const Params& p, int threads, hipStream_t stream, in
 // gives every workgroup a long run of key tiles; short causal sequences keep
 // the direct-to-LDS kernel, whose smaller workgroups spread the little work
 // of the short query tiles over more CUs (measured on MI355X).
-bool use_pipe(int N, bool causal) {
-#if FA_16BIT_KERNEL == 3
-  return !causal || N >= FA_PIPE_MIN_N;
-#else
-  (void)N, (void)causal;
-  return FA_16BIT_KERNEL == 2;
-#endif
-}
+bool use_pipe(int N, bool causal) { return !causal || N >= FA_PIPE_MIN_N; }
+
+// Workgroups per (batch, head) of the pipelined kernel: one per query tile,
+// or per folded pair of causal query tiles.
+int pipe_units(const Params& p, bool causal) { return causal ? (p.n_qt + 1) / 2 : p.n_qt; }
 
 template <class E, int D, bool C>
 hipError_t launch_16bit(const Params& p, hipStream_t s) {
-  if (p.win_left >= 0 || p.win_right >= 0) {
-    if (FA_WIN_PIPE && use_pipe(p.N, C))
-      return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false, false, D, true>,
-                    p, FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
-    return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C, true>, p,
+  if (p.win_left >= 0 || p.win_right >= 0)
+    return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, C, true>, p,
                   FA_DMA_WAVES * 64, s);
-  }
   if (use_pipe(p.N, C))
-    return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false>, p,
-                  FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
-#if FA_16BIT_KERNEL == 0
-  return launch(attn_fwd_16bit<E, D, kWaves, FA_KEY_TILE, C>, p, kWaves * 64, s);
-#else
-  return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C>, p,
-                FA_DMA_WAVES * 64, s);
-#endif
+    return launch(attn_fwd_pipe<E, D, FA_WIDE_WAVES, C, false>, p, FA_WIDE_WAVES * 64, s,
+                  pipe_units(p, C));
+  return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, C>, p, FA_DMA_WAVES * 64, s);
 }
 
 // Packed batches take the kernel a single sequence of the longest length
@@ -3155,9 +2238,9 @@ hipError_t launch_16bit(const Params& p, hipStream_t s) {
 template <class E, int D, bool C>
 hipError_t launch_16bit_varlen(const Params& p, hipStream_t s) {
   if (use_pipe(p.N, C))
-    return launch(attn_fwd_pipe<E, D, FA_WIDE_GROUPS, FA_WIDE_WAVES, FA_PIPE_NBUF, C, false, true>,
-                  p, FA_WIDE_WAVES * 64, s, C ? (p.n_qt + 1) / 2 : p.n_qt);
-  return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, FA_NBUF, C, false, true>, p,
+    return launch(attn_fwd_pipe<E, D, FA_WIDE_WAVES, C, false, true>, p, FA_WIDE_WAVES * 64, s,
+                  pipe_units(p, C));
+  return launch(attn_fwd_16bit_dma<E, D, FA_KEY_TILE, FA_DMA_WAVES, C, false, true>, p,
                 FA_DMA_WAVES * 64, s);
 }
 
@@ -3169,8 +2252,8 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
     case Kind::F16: return launch_16bit<F16, D, C>(p, s);
     case Kind::FP8:
       if (use_pipe(p.N, C))
-        return launch(attn_fwd_pipe<Bf16, D, 1, FA_WIDE_WAVES, 2, C, true>, p, FA_WIDE_WAVES * 64, s,
-                      C ? (p.n_qt + 1) / 2 : p.n_qt);
+        return launch(attn_fwd_pipe<Bf16, D, FA_WIDE_WAVES, C, true>, p, FA_WIDE_WAVES * 64, s,
+                      pipe_units(p, C));
       return launch(attn_fwd_fp8<D, kWaves, FA_KEY_TILE, C>, p, T, s);
     case Kind::F32: return launch(attn_fwd_f32<D, kWaves, 32, C>, p, T, s);
   }
@@ -3182,38 +2265,29 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
 int rows_per_block(Kind kind, int d, int N, bool causal, bool window) {
   if (d == 256) {
     if ((kind != Kind::BF16 && kind != Kind::F16) || window) return 0;
-    return FA_D256_PIPE && use_pipe(N, causal) ? FA_WIDE_WAVES * 32 : 4 * 32;
+    return use_pipe(N, causal) ? FA_WIDE_WAVES * 32 : 4 * 32;
   }
   if (d != 64 && d != 128) return 0;
-  if (window) {
-    if (kind != Kind::BF16 && kind != Kind::F16) return 0;
-    return FA_WIN_PIPE && use_pipe(N, causal) ? FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS : FA_DMA_WAVES * 32;
-  }
+  if (window) return kind == Kind::BF16 || kind == Kind::F16 ? FA_DMA_WAVES * 32 : 0;
+  if (kind == Kind::BF16 || kind == Kind::F16)
+    return use_pipe(N, causal) ? FA_WIDE_WAVES * 32 : FA_DMA_WAVES * 32;
   if (kind == Kind::FP8 && use_pipe(N, causal)) return FA_WIDE_WAVES * 32;
-  if (kind == Kind::BF16 || kind == Kind::F16) {
-    if (use_pipe(N, causal)) return FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS;
-#if FA_16BIT_KERNEL != 0
-    return FA_DMA_WAVES * 32;
-#endif
-  }
   return kWaves * 32;
 }
 
 hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStream_t stream) {
   if (d == 256) {
-#if FA_D256_PIPE
     // the pipelined kernel on 128-column slices of V and O (two workgroups
     // per query tile, or per folded pair of causal tiles)
     if ((kind == Kind::BF16 || kind == Kind::F16) && use_pipe(p.N, causal)) {
-      const int units = 2 * (causal ? (p.n_qt + 1) / 2 : p.n_qt);
+      const int units = 2 * pipe_units(p, causal);
       constexpr int T = FA_WIDE_WAVES * 64;
       if (kind == Kind::BF16)
-        return causal ? launch(attn_fwd_pipe<Bf16, 256, 1, FA_WIDE_WAVES, 2, true, false, false, 128>, p, T, stream, units)
-                      : launch(attn_fwd_pipe<Bf16, 256, 1, FA_WIDE_WAVES, 2, false, false, false, 128>, p, T, stream, units);
-      return causal ? launch(attn_fwd_pipe<F16, 256, 1, FA_WIDE_WAVES, 2, true, false, false, 128>, p, T, stream, units)
-                    : launch(attn_fwd_pipe<F16, 256, 1, FA_WIDE_WAVES, 2, false, false, false, 128>, p, T, stream, units);
+        return causal ? launch(attn_fwd_pipe<Bf16, 256, FA_WIDE_WAVES, true, false, false, 128>, p, T, stream, units)
+                      : launch(attn_fwd_pipe<Bf16, 256, FA_WIDE_WAVES, false, false, false, 128>, p, T, stream, units);
+      return causal ? launch(attn_fwd_pipe<F16, 256, FA_WIDE_WAVES, true, false, false, 128>, p, T, stream, units)
+                    : launch(attn_fwd_pipe<F16, 256, FA_WIDE_WAVES, false, false, false, 128>, p, T, stream, units);
     }
-#endif
     // two workgroups (column halves of O) per query tile
     const long long grid = 2LL * p.B * p.H * p.n_qt;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -3231,7 +2305,7 @@ hipError_t launch_forward(Kind kind, int d, bool causal, const Params& p, hipStr
 }
 
 int varlen_rows_per_block(int max_seqlen, bool causal) {
-  return use_pipe(max_seqlen, causal) ? FA_WIDE_WAVES * 32 * FA_WIDE_GROUPS : FA_DMA_WAVES * 32;
+  return use_pipe(max_seqlen, causal) ? FA_WIDE_WAVES * 32 : FA_DMA_WAVES * 32;
 }
 
 hipError_t launch_forward_varlen(Kind kind, int d, bool causal, const Params& p,
@@ -3297,24 +2371,11 @@ hipError_t launch_backward_t(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipLaunchKernel((const void*)attn_bwd_prep<typename E::T, D>, dim3((unsigned)g_prep),
                                  dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
-#if FA_BWD_DMA
-  const void* kdq = FA_BWD_DQ_PIPE ? (const void*)attn_bwd_dq_pipe<E, D, C>
-                                   : (const void*)attn_bwd_dq_dma<E, D, C>;
-  const void* kkv = (const void*)attn_bwd_dkdv_dma<E, D, C>;
-#else
-  const void* kdq = (const void*)attn_bwd_dq<E, D, C>;
-  const void* kkv = (const void*)attn_bwd_dkdv<E, D, C>;
-#endif
-  e = hipLaunchKernel(kdq, dim3((unsigned)g_dq), dim3(kBwdWaves * 64), args, 0, stream);
-  if (e != hipSuccess) return e;
-#if FA_BWD_DMA && FA_BWD_SPLIT
-  // dV and dK in passes of their own: one accumulator set each
-  e = hipLaunchKernel((const void*)attn_bwd_dkdv_dma<E, D, C, 1>, dim3((unsigned)g_kv),
+  e = hipLaunchKernel((const void*)attn_bwd_dq_dma<E, D, C>, dim3((unsigned)g_dq),
                       dim3(kBwdWaves * 64), args, 0, stream);
   if (e != hipSuccess) return e;
-  kkv = (const void*)attn_bwd_dkdv_dma<E, D, C, 2>;
-#endif
-  return hipLaunchKernel(kkv, dim3((unsigned)g_kv), dim3(kBwdWaves * 64), args, 0, stream);
+  return hipLaunchKernel((const void*)attn_bwd_dkdv_dma<E, D, C>, dim3((unsigned)g_kv),
+                         dim3(kBwdWaves * 64), args, 0, stream);
 }
 template <class E>
 hipError_t launch_backward_e(int d, bool causal, const BwdParams& p, hipStream_t s) {

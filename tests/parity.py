@@ -81,3 +81,51 @@ def sampled_rows(spec, rng, per_head=48, extra=None):
         fixed |= {int(r) for r in extra if 0 <= r < N}
     rnd = rng.choice(N, size=min(N, per_head), replace=False)
     return np.array(sorted(fixed | set(int(r) for r in rnd)), dtype=np.int64)
+
+
+def worker_count() -> int:
+    """Host threads for oracle work: this process's CPU share, at most 16."""
+    import os
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(16, n))
+
+
+def every_element_errors(w, o, lse, say_every=8):
+    """max|dO|, mean|dO| over all B*H*N*d elements and max|dLSE| of the
+    library's (o, lse) against the float64 oracle, computed head by head
+    (a pool of threads, each head's oracle with one BLAS thread) so that
+    memory stays bounded at the full workload sizes."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    s = w.spec
+    q, k, v = w.exact()
+    kl = w.key_len_or_none()
+    pairs = [(b, h) for b in range(s.B) for h in range(s.H)]
+
+    def one(bh):
+        b, h = bh
+        g = h // (s.H // s.kv_heads)
+        o_ref, lse_ref = oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1],
+                                                  v[b:b + 1, g:g + 1], s.scale, s.causal,
+                                                  None if kl is None else kl[b:b + 1])
+        d = np.abs(o[b, h] - o_ref[0, 0])
+        fin = np.isfinite(lse_ref[0, 0])
+        same_inf = bool(np.array_equal(np.isfinite(lse[b, h]), fin)
+                        and np.all(lse[b, h][~fin] == lse_ref[0, 0][~fin]))
+        dl = float(np.abs(lse[b, h][fin] - lse_ref[0, 0][fin]).max()) if fin.any() else 0.0
+        return float(d.max()), float(d.sum()), d.size, dl, same_inf
+
+    mx, total, count, dl, same = 0.0, 0.0, 0, 0.0, True
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=worker_count()) as ex:
+        for i, r in enumerate(ex.map(one, pairs)):
+            mx, total, count = max(mx, r[0]), total + r[1], count + r[2]
+            dl, same = max(dl, r[3]), same and r[4]
+            if (i + 1) % say_every == 0 or i + 1 == len(pairs):
+                say(f"  oracle heads {i + 1}/{len(pairs)}: max|dO|={mx:.3e} "
+                    f"mean|dO|={total / count:.3e} max|dLSE|={dl:.3e}")
+    return mx, total / max(1, count), dl, same

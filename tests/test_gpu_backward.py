@@ -95,3 +95,56 @@ def test_backward_rejects_bad_dtype_and_workspace():
         fa.fa_bwd(qb, kb, vb, ob, qb, lseb, *gb, small, 0.125)
     torch.cuda.synchronize()
     assert all(torch.all(x == 3.0) for x in gb)
+
+
+def test_backward_full_benched_shape():
+    """The shape the benchmark times (B1 H32 N8192 d128 causal bf16, the long
+    workload's inputs with its outlier keys): every element of dQ, dK and dV
+    against the float64 backward oracle, head by head."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from parity import worker_count
+
+    w = W.draw(W.SPECS["long_causal_bf16"])
+    s = w.spec
+    say(f"case bwd full shape B{s.B} H{s.H} N{s.N} d{s.d} causal={s.causal} seed={s.seed}")
+    rng = np.random.default_rng(s.seed + 1)
+    do32 = rng.standard_normal((s.B, s.H, s.N, s.d)).astype(np.float32)
+    do = torch.from_numpy(do32).to(torch.bfloat16)
+    q, k, v, dod = (t.to(DEV) for t in (w.q, w.k, w.v, do))
+    o, lse = fa.fwd(q, k, v, scale=s.scale, causal=s.causal)
+    grads = fa.bwd(q, k, v, o, lse, dod, scale=s.scale, causal=s.causal)
+    torch.cuda.synchronize()
+    got = [g.double().cpu().numpy() for g in grads]
+    del grads
+    qe, ke, ve = w.exact()
+    dod64 = do.double().numpy()
+
+    def one(h):
+        ref = oracle.attention_backward(qe[:, h:h + 1], ke[:, h:h + 1], ve[:, h:h + 1],
+                                        dod64[:, h:h + 1], s.scale, s.causal)
+        out = []
+        for g, r in zip(got, ref):
+            d = np.abs(g[:, h:h + 1] - r)
+            out.append((float(d.max()), float(d.sum()), float(np.abs(r).max()),
+                        float(np.abs(r).sum()), d.size))
+        return out
+
+    acc = [[0.0, 0.0, 0.0, 0.0, 0] for _ in range(3)]
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=min(8, worker_count())) as ex:
+        for i, res in enumerate(ex.map(one, range(s.H))):
+            for a, r in zip(acc, res):
+                a[0], a[1], a[2], a[3], a[4] = (max(a[0], r[0]), a[1] + r[1], max(a[2], r[2]),
+                                                a[3] + r[3], a[4] + r[4])
+            if (i + 1) % 8 == 0:
+                say(f"  oracle heads {i + 1}/{s.H}")
+    for name, (mx, sd, mr, sr, n) in zip(("dQ", "dK", "dV"), acc):
+        rel_max = mx / max(1.0, mr)
+        rel_mean = (sd / n) / max(1e-3, sr / n)
+        say(f"  full shape {name}: max|d|={mx:.3e} (rel {rel_max:.3e}) mean|d|={sd / n:.3e} "
+            f"(rel {rel_mean:.3e}) max|ref|={mr:.3e}")
+        assert np.isfinite(mx), f"{name}: non-finite"
+        assert rel_max <= TOL_MAX, f"{name}: max rel {rel_max}"
+        assert rel_mean <= TOL_MEAN, f"{name}: mean rel {rel_mean}"
