@@ -1,7 +1,7 @@
 """Exact IO-aware attention forward for AMD Instinct MI355X (gfx950).
 
 Python face of libfa (include/fa.h). ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_gqa`` /
-``fa_fwd_window`` / ``fa_fwd_varlen`` / ``fa_fwd_decode`` / ``fa_bwd`` marshal torch tensors' device pointers and the current stream
+``fa_fwd_window`` / ``fa_fwd_varlen`` / ``fa_fwd_decode`` / ``fa_fwd_decode_noalloc`` / ``fa_bwd`` marshal torch tensors' device pointers and the current stream
 into the C entry points of the same names; ``fwd`` (and its positional twin ``forward``) additionally
 allocates O and LSE. Nothing here computes any part of the attention.
 """
@@ -183,13 +183,8 @@ def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
     return forward(q, k, v, scale, causal, key_len, descale, stream, window)
 
 
-def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool = False,
-                  key_len: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Enqueue fa_fwd_decode: q [B, H, Nq, d], k, v [B, H_kv, Nk, d] (16-bit),
-    o like q, lse float32 [B, H, Nq], workspace a contiguous device tensor of at
-    least decode_workspace_bytes(...) bytes."""
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse),
-                    ("workspace", workspace)):
+def _check_decode(q, k, v, o, lse, key_len, tensors):
+    for name, t in tensors:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
@@ -206,11 +201,33 @@ def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool = False
     if key_len is not None and (not key_len.is_cuda or key_len.dtype != torch.int32
                                 or key_len.shape != (B,) or not key_len.is_contiguous()):
         raise ValueError("key_len must be a contiguous device int32 tensor of shape [B]")
+    return B, H, Nq, d
+
+
+def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool = False,
+                  key_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue fa_fwd_decode: q [B, H, Nq, d], k, v [B, H_kv, Nk, d] (16-bit),
+    o like q, lse float32 [B, H, Nq], workspace a contiguous device tensor of at
+    least decode_workspace_bytes(...) bytes."""
+    B, H, Nq, d = _check_decode(q, k, v, o, lse, key_len,
+                                (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse),
+                                 ("workspace", workspace)))
     nbytes = workspace.numel() * workspace.element_size()
     _lib._check(_lib.fa_fwd_decode_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
                                        k.shape[1], Nq, k.shape[2], d, scale, causal,
                                        _ptr(key_len), _DTYPE[q.dtype], _ptr(workspace), nbytes,
                                        _stream(stream)))
+
+
+def fa_fwd_decode_noalloc(q, k, v, o, lse, scale: float, causal: bool = False,
+                          key_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue fa_fwd_decode_noalloc: fa_fwd_decode with the partial results in
+    the library's own device scratch (no workspace argument)."""
+    B, H, Nq, d = _check_decode(q, k, v, o, lse, key_len,
+                                (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)))
+    _lib._check(_lib.fa_fwd_decode_noalloc_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B,
+                                               H, k.shape[1], Nq, k.shape[2], d, scale, causal,
+                                               _ptr(key_len), _DTYPE[q.dtype], _stream(stream)))
 
 
 def decode(q, k, v, *, scale: float, causal: bool = False, key_len=None,

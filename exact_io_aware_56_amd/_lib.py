@@ -16,6 +16,7 @@ FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_decode", "fa_decode_workspace_bytes",
+            "fa_fwd_decode_noalloc",
             "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_fwd_varlen", "fa_status_str",
             "fa_abi_version", "fa_last_error")
 
@@ -46,6 +47,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
     lib.fa_fwd_decode.restype = i
+    lib.fa_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_fwd_decode_noalloc.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
@@ -106,6 +109,12 @@ def fa_fwd_decode_raw(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, key
     return load().fa_fwd_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, float(scale),
                                 int(causal), key_len, int(dtype), workspace,
                                 int(workspace_bytes), stream)
+
+
+def fa_fwd_decode_noalloc_raw(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, key_len,
+                              dtype, stream) -> int:
+    return load().fa_fwd_decode_noalloc(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, float(scale),
+                                        int(causal), key_len, int(dtype), stream)
 
 
 def bwd_workspace_bytes(B, H, N) -> int:

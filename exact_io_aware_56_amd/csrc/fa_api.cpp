@@ -169,12 +169,16 @@ bool decode_shape(int B, int H, int H_kv, int Nq, int Nk, int d, DecodeShape& sh
   return true;
 }
 
+// own_scratch: the partial results go to the library's device scratch
+// (fa_fwd_decode_noalloc) instead of the caller's workspace, which is then
+// ignored.
 int decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
            int H_kv, int Nq, int Nk, int d, float scale, int causal, const int32_t* key_len,
-           int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+           int dtype, void* workspace, size_t workspace_bytes, void* stream,
+           bool own_scratch = false) {
   g_last_error[0] = '\0';
   if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  if (!workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+  if (!own_scratch && !workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1)
     return fail(FA_ERR_INVALID_ARG, "B, H, Nq, Nk and d must be >= 1");
   if (H_kv < 1 || H % H_kv != 0) return fail(FA_ERR_INVALID_ARG, "H_kv must be >= 1 and divide H");
@@ -182,7 +186,7 @@ int decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int
     return fail(FA_ERR_INVALID_ARG, "dtype is not a fa_dtype value");
   if (!positive_finite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
-      !aligned(workspace, 16))
+      (!own_scratch && !aligned(workspace, 16)))
     return fail(FA_ERR_INVALID_ARG, "Q, K, V, O and the workspace must be 16-byte aligned");
   if (!aligned(LSE, 4) || (key_len && !aligned(key_len, 4)))
     return fail(FA_ERR_INVALID_ARG, "LSE and key_len must be 4-byte aligned");
@@ -196,8 +200,20 @@ int decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
   if ((long long)Nk * d * 2 >= (1LL << 30))
     return fail(FA_ERR_UNSUPPORTED, "one head's Nk x d tensor must be under 1 GiB");
-  if ((long long)workspace_bytes < sh.ws_bytes)
+  if (own_scratch) {
+    if (sh.ws_bytes > (long long)FA_DECODE_NOALLOC_MAX_BYTES)
+      return fail(FA_ERR_UNSUPPORTED,
+                  "decode partial results exceed the library's 8 MiB device scratch "
+                  "(fa_decode_workspace_bytes() > FA_DECODE_NOALLOC_MAX_BYTES); use fa_fwd_decode");
+    const hipError_t e = fa::decode_scratch(&workspace);
+    if (e != hipSuccess) {
+      snprintf(g_last_error, sizeof g_last_error, "device scratch lookup failed: %s",
+               hipGetErrorString(e));
+      return FA_ERR_HIP;
+    }
+  } else if ((long long)workspace_bytes < sh.ws_bytes) {
     return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_decode_workspace_bytes()");
+  }
 
   fa::DecodeParams p;
   p.q = Q;
@@ -336,6 +352,14 @@ int fa_fwd_decode(const void* Q, const void* K, const void* V, void* O, float* L
                   void* stream) {
   return decode(Q, K, V, O, LSE, B, H, H_kv, Nq, Nk, d, scale, causal, key_len, dtype, workspace,
                 workspace_bytes, stream);
+}
+
+int fa_fwd_decode_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                          int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                          const int32_t* key_len, int dtype, void* stream) {
+  static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_MAX_BYTES, "scratch size");
+  return decode(Q, K, V, O, LSE, B, H, H_kv, Nq, Nk, d, scale, causal, key_len, dtype, nullptr, 0,
+                stream, true);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N) { return (size_t)bwd_workspace(B, H, N); }

@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -2391,6 +2392,33 @@ hipError_t launch_backward(Kind kind, int d, bool causal, const BwdParams& p, hi
   if (kind == Kind::BF16) return launch_backward_e<Bf16>(d, causal, p, stream);
   if (kind == Kind::F16) return launch_backward_e<F16>(d, causal, p, stream);
   return hipErrorInvalidValue;
+}
+
+// Device scratch of fa_fwd_decode_noalloc: a fixed array in the code object,
+// one copy on every device the library runs on, held until the process ends.
+// Host code never names it as an address: the device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and kept
+// per device; kernels receive that address like a caller's workspace.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = ptr;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(Kind kind, int d, bool causal, const DecodeParams& p, hipStream_t stream) {

@@ -102,4 +102,10 @@ hipError_t launch_backward(Kind kind, int d, bool causal, const BwdParams& p, hi
 // Enqueue the split pass and the merge on `stream` (16-bit kinds only).
 hipError_t launch_decode(Kind kind, int d, bool causal, const DecodeParams& p, hipStream_t stream);
 
+// Bytes of the device scratch behind fa_fwd_decode_noalloc.
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+
+// The current device's address of that scratch (looked up once per device).
+hipError_t decode_scratch(void** out);
+
 }  // namespace fa

@@ -26,8 +26,10 @@
  *   - LSE is a device pointer to float [B, H, N], 4-byte aligned.
  *   - key_len is NULL or a device pointer to int32 [B]; values are clamped to
  *     [0, N] on the device, so any int32 value is accepted.
- *   - The caller owns every buffer. The library allocates no memory of any
- *     kind and keeps no global state; calls are re-entrant and thread-safe.
+ *   - The caller owns every buffer. The library allocates no memory and
+ *     keeps no state but a per-thread error string, except the one fixed
+ *     device array behind fa_fwd_decode_noalloc (see there); every other
+ *     call is re-entrant and thread-safe.
  *   - Calls are asynchronous: they enqueue work on `stream` (a hipStream_t;
  *     NULL = the null stream) and return. Results are ready once the stream
  *     is synchronised. A fault inside the kernel surfaces at the caller's
@@ -46,8 +48,8 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd; 5: fa_fwd_window;
-                             6: fa_fwd_varlen */
+#define FA_ABI_VERSION 7  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd; 5: fa_fwd_window;
+                             6: fa_fwd_varlen; 7: fa_fwd_decode_noalloc */
 
 typedef enum {
   FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
@@ -227,6 +229,30 @@ int fa_fwd_decode(const void* Q, const void* K, const void* V, void* O, float* L
  * products out of range).
  */
 size_t fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
+
+/*
+ * fa_fwd_decode_noalloc -- fa_fwd_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, arguments and results, with
+ * the per-chunk partial results held in the library's own device scratch
+ * instead of a caller workspace. The call itself allocates nothing.
+ *
+ * The scratch is one fixed array of FA_DECODE_NOALLOC_MAX_BYTES in the
+ * library's code object: each device the library runs on holds its own copy
+ * from the first kernel launch until the process ends. Sizes whose
+ * fa_decode_workspace_bytes() exceed FA_DECODE_NOALLOC_MAX_BYTES return
+ * FA_ERR_UNSUPPORTED (use fa_fwd_decode with a workspace). Every call on a
+ * device shares that device's scratch and leaves its partial results there:
+ * calls that may overlap in time on one device (different streams or host
+ * threads) race, and must be ordered by the caller. Nothing in the scratch
+ * needs to start at any value. Errors as fa_fwd_decode (no workspace
+ * checks), plus FA_ERR_HIP if the scratch's device address cannot be looked
+ * up.
+ */
+#define FA_DECODE_NOALLOC_MAX_BYTES (8u << 20)
+int fa_fwd_decode_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                          const int32_t* key_len, int dtype, void* stream);
 
 /*
  * fa_bwd -- gradients of fa_fwd / fa_fwd_gqa with respect to Q, K and V.

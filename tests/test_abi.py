@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 6
+    assert lib.fa_abi_version() == 7
     assert _lib.status_name(0) == "FA_OK"
     assert _lib.status_name(-1) == "FA_ERR_INVALID_ARG"
     assert _lib.status_name(-2) == "FA_ERR_UNSUPPORTED"
@@ -119,6 +119,37 @@ def decode_call(**kw):
 def test_decode_entry_point_rejects_bad_arguments(kw, status):
     assert decode_call(**kw) == status
     assert _lib.load().fa_last_error().decode() != ""
+
+
+def noalloc_call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=8, H_kv=2, Nq=1, Nk=4096, d=128, scale=0.1,
+             causal=1, key_len=None, dtype=2, stream=None)
+    a.update(kw)
+    return _lib.fa_fwd_decode_noalloc_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                          a["H"], a["H_kv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                          a["causal"], a["key_len"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(Nq=0), -1), (dict(H_kv=3), -1), (dict(scale=math.nan), -1),
+    (dict(o=P + 8), -1), (dict(dtype=0), -2), (dict(d=256), -2),
+    # partial results beyond the library's scratch: 64*32*64 rows x (128+1) floats
+    (dict(B=64, H=32, H_kv=8, Nq=64, Nk=8192), -2),
+])
+def test_noalloc_decode_rejects_bad_arguments(kw, status):
+    assert noalloc_call(**kw) == status
+    assert _lib.load().fa_last_error().decode() != ""
+
+
+def test_noalloc_decode_limit_is_the_workspace_size():
+    limit = 8 << 20
+    header = open(HEADER).read()
+    assert re.search(r"#define FA_DECODE_NOALLOC_MAX_BYTES \(8u << 20\)", header)
+    assert _lib.decode_workspace_bytes(64, 32, 8, 64, 8192, 128) > limit
+    assert noalloc_call(B=64, H=32, H_kv=8, Nq=64, Nk=8192) == -2
+    assert "FA_DECODE_NOALLOC_MAX_BYTES" in _lib.load().fa_last_error().decode()
+    # the decode workload of the benchmark fits
+    assert _lib.decode_workspace_bytes(16, 32, 8, 1, 16384, 128) <= limit
 
 
 def test_decode_workspace_size():
