@@ -231,6 +231,11 @@ def _cpu_baseline(w, budget_s: float, threads: int):
                       f"float64, {dt:.2f} s wall"}
 
 
+def workload_dtype(name: str) -> str:
+    import workloads as W
+    return W.SPECS[name].dtype if name in W.SPECS else ""
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +245,9 @@ def main(argv=None):
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV) of the workload instead of the "
                          "forward; FLOP counted as 2.5x the forward's (five N^2 d products)")
+    ap.add_argument("--p8", action="store_true",
+                    help="fp8 workloads: time fa_fwd_fp8_p8 (P rounded to e4m3 for the P V "
+                         "product, both products on the fp8 matrix cores)")
     ap.add_argument("--N", type=int, default=0,
                     help="override the workload's sequence length (HBM scaling runs); "
                          "such a line is not the headline measurement")
@@ -253,6 +261,9 @@ def main(argv=None):
                          "its HBM counters calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args(argv)
 
+    if args.p8 and workload_dtype(args.workload) != "fp8":
+        print(json.dumps({"error": "--p8 applies to fp8 workloads"}))
+        return 2
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; "
                                    "multi-GPU runs are not supported (use --gpus 1)"}))
@@ -317,6 +328,9 @@ def main(argv=None):
             fa.fa_fwd_decode(q, k, v, o, lse, ws, spec.scale, spec.causal, kl, stream=stream)
         elif spec.kv_heads != spec.H:
             fa.fa_fwd_gqa(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
+        elif spec.dtype == "fp8" and args.p8:
+            fa.fa_fwd_fp8_p8(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale,
+                             stream=stream)
         elif spec.dtype == "fp8":
             fa.fa_fwd_fp8(q, k, v, o, lse, spec.scale, spec.causal, kl, *w.descale, stream=stream)
         else:
@@ -389,7 +403,8 @@ def main(argv=None):
     value = flop / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[spec.dtype]
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
-    traffic = measured_traffic(spec.name) if default_n and not args.backward else None
+    prof_name = spec.name + ("_p8" if args.p8 else "")
+    traffic = measured_traffic(prof_name) if default_n and not args.backward else None
     exps = w.exps()
     if spec.is_decode:
         # HBM-bound: the roofline is bytes moved, the two kernels of a step
@@ -425,6 +440,7 @@ def main(argv=None):
                 "sequences": spec.B, "rows": int(w.q.shape[1]),
                 "lengths": "U{%d..%d}" % spec.key_len_range, "max_seqlen": spec.N},
             "outlier_keys_frac": spec.outlier_frac, "seed": spec.seed,
+            "p_e4m3": bool(args.p8) if spec.dtype == "fp8" else None,
             "settle_launches": settle,
             "spread_sample_steps": len(per),
             "launch_ms_p10": round(per[len(per) // 10], 5),
@@ -448,7 +464,7 @@ def main(argv=None):
                     "frac": round(exps / (avg_launch_ms * 1e-3) / 1e12 / EXP_PEAK_T, 4)},
         },
     }
-    counters = sq_counters(spec.name) if default_n and not args.backward else None
+    counters = sq_counters(prof_name) if default_n and not args.backward else None
     if counters is not None:
         result["counters"] = counters
     if w.key_len is not None and (not spec.causal or spec.is_decode):

@@ -85,6 +85,19 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool = False,
                                     _stream(stream)))
 
 
+def fa_fwd_fp8_p8(q8, k8, v8, o, lse, scale: float, causal: bool = False,
+                  key_len: Optional[torch.Tensor] = None, q_descale: float = 1.0,
+                  k_descale: float = 1.0, v_descale: float = 1.0, stream=None) -> None:
+    """Enqueue fa_fwd_fp8_p8 (as fa_fwd_fp8, with P rounded to e4m3 for P V)."""
+    if q8.dtype != torch.float8_e4m3fn:
+        raise ValueError("fa_fwd_fp8_p8 takes float8_e4m3fn inputs")
+    _check_inputs(q8, k8, v8, o, lse, key_len)
+    B, H, N, d = q8.shape
+    _lib._check(_lib.fa_fwd_fp8_p8_raw(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, H, N,
+                                       d, scale, causal, _ptr(key_len), q_descale, k_descale,
+                                       v_descale, _stream(stream)))
+
+
 def fa_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool = False,
                key_len: Optional[torch.Tensor] = None, q_descale: float = 1.0,
                k_descale: float = 1.0, v_descale: float = 1.0, stream=None) -> None:
@@ -152,9 +165,12 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float, causal: bo
 
 def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
             descale: Tuple[float, float, float] = (1.0, 1.0, 1.0),
-            stream=None, window=None) -> Tuple[torch.Tensor, torch.Tensor]:
+            stream=None, window=None, p8: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Allocate O and LSE on q's device and run the forward; returns (O, LSE).
-    k and v with fewer heads than q take the grouped entry point."""
+    k and v with fewer heads than q take the grouped entry point; p8 (fp8
+    inputs only) takes fa_fwd_fp8_p8."""
+    if p8 and (q.dtype != torch.float8_e4m3fn or window is not None or k.shape[1] != q.shape[1]):
+        raise ValueError("p8 takes fp8 inputs with one K/V head per query head and no window")
     B, H, N, d = q.shape
     o = torch.empty((B, H, N, d), dtype=out_dtype(q.dtype), device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -162,6 +178,8 @@ def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
         fa_fwd_window(q, k, v, o, lse, scale, causal, window, key_len, *descale, stream=stream)
     elif k.dim() == 4 and k.shape[1] != H:
         fa_fwd_gqa(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
+    elif p8:
+        fa_fwd_fp8_p8(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
     elif q.dtype == torch.float8_e4m3fn:
         fa_fwd_fp8(q, k, v, o, lse, scale, causal, key_len, *descale, stream=stream)
     else:
@@ -171,7 +189,7 @@ def forward(q, k, v, scale: float, causal: bool = False, key_len=None,
 
 def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
         descale: Tuple[float, float, float] = (1.0, 1.0, 1.0),
-        stream=None, window=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        stream=None, window=None, p8: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """softmax(scale * Q K^T + mask) V and its row log-sum-exp, as (O, LSE).
 
     Keyword-only form of ``forward``. q, k, v: contiguous device tensors
@@ -179,8 +197,9 @@ def fwd(q, k, v, *, scale: float, causal: bool = False, key_len=None,
     or k, v of [B, H_kv, N, d] with H_kv dividing H (grouped K/V heads);
     key_len: optional device int32 [B] of valid key counts. O has q's dtype
     (bfloat16 for fp8 inputs); LSE is float32 [B, H, N], natural log.
+    p8: fp8 inputs with P rounded to e4m3 for the P V product.
     """
-    return forward(q, k, v, scale, causal, key_len, descale, stream, window)
+    return forward(q, k, v, scale, causal, key_len, descale, stream, window, p8)
 
 
 def _check_decode(q, k, v, o, lse, key_len, tensors):

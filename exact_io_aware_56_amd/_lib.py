@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_decode", "fa_decode_workspace_bytes",
+EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_p8", "fa_fwd_gqa", "fa_fwd_decode", "fa_decode_workspace_bytes",
             "fa_fwd_decode_noalloc",
             "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_fwd_varlen", "fa_status_str",
             "fa_abi_version", "fa_last_error")
@@ -42,6 +42,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, f, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_fp8_p8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, f, f, vp]
+    lib.fa_fwd_fp8_p8.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, f, f, f, vp]
     lib.fa_fwd_gqa.restype = i
     sz = ctypes.c_size_t
@@ -92,6 +94,12 @@ def fa_fwd_fp8_raw(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, qd, kd, 
                    stream) -> int:
     return load().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), key_len,
                              float(qd), float(kd), float(vd), stream)
+
+
+def fa_fwd_fp8_p8_raw(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, qd, kd, vd,
+                      stream) -> int:
+    return load().fa_fwd_fp8_p8(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), key_len,
+                                float(qd), float(kd), float(vd), stream)
 
 
 def fa_fwd_gqa_raw(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, dtype, qd, kd, vd,

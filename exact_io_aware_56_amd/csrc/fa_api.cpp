@@ -27,7 +27,8 @@ bool positive_finite(float x) { return isfinite(x) && x > 0.0f; }
 
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
             int H_kv, int N, int d, float scale, int causal, const int32_t* key_len, int dtype,
-            float qd, float kd, float vd, void* stream, int win_left = -1, int win_right = -1) {
+            float qd, float kd, float vd, void* stream, int win_left = -1, int win_right = -1,
+            bool p8 = false) {
   g_last_error[0] = '\0';
   if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N and d must be >= 1");
@@ -55,7 +56,7 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   const long long head_bytes = (long long)N * d * (dtype == FA_DTYPE_FP32 ? 4 : dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2);
   if (head_bytes >= (1LL << 30)) return fail(FA_ERR_UNSUPPORTED, "one head's N x d tensor must be under 1 GiB");
 
-  const fa::Kind kind = static_cast<fa::Kind>(dtype);
+  const fa::Kind kind = p8 ? fa::Kind::FP8_P8 : static_cast<fa::Kind>(dtype);
   const int rows = fa::rows_per_block(kind, d, N, causal != 0, window);
   fa::Params p;
   p.q = Q;
@@ -331,6 +332,13 @@ int fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, void* O_bf16, flo
                float q_descale, float k_descale, float v_descale, void* stream) {
   return forward(Q8, K8, V8, O_bf16, LSE, B, H, H, N, d, scale, causal, key_len, FA_DTYPE_FP8_E4M3,
                  q_descale, k_descale, v_descale, stream);
+}
+
+int fa_fwd_fp8_p8(const void* Q8, const void* K8, const void* V8, void* O_bf16, float* LSE, int B,
+                  int H, int N, int d, float scale, int causal, const int32_t* key_len,
+                  float q_descale, float k_descale, float v_descale, void* stream) {
+  return forward(Q8, K8, V8, O_bf16, LSE, B, H, H, N, d, scale, causal, key_len, FA_DTYPE_FP8_E4M3,
+                 q_descale, k_descale, v_descale, stream, -1, -1, true);
 }
 
 int fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,

@@ -52,6 +52,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -486,12 +487,13 @@ __device__ __forceinline__ void epilogue(const Params& p, const RowRange& rr, in
 // half written cost extra memory writes.
 // D: columns this call writes (one row of the stage); DO: elements per row of
 // O in memory, the columns starting at col0 (a column slice when DO > D); LSE
-// is written only when lse is set.
+// is written only when lse is set, from l_lse (a lane-partial sum like l)
+// when that is given instead of l.
 template <class OutT, int D, int DB, int DO = D>
 __device__ __forceinline__ void epilogue_staged(const Params& p, int bh, int row0, int lane,
                                                 float m, float l, const f32x16 (&o)[DB],
                                                 unsigned char* stage, int col0 = 0,
-                                                bool lse = true) {
+                                                bool lse = true, float l_lse = -1.0f) {
   typedef OutT v4 __attribute__((ext_vector_type(4)));
   constexpr int RB = D * 2, CPR = D / 8;  // bytes and 16-byte slots per row
   // Addresses come from an opaque copy of the lane index: computed here, not
@@ -522,8 +524,12 @@ __device__ __forceinline__ void epilogue_staged(const Params& p, int bh, int row
     const i32x4 v = *(FA_LDS const i32x4*)(stage + r * RB + ((c ^ (r % CPR)) << 4));
     if (row0 + r < p.N) *(i32x4*)((OutT*)p.o + ((size_t)bh * p.N + row0 + r) * DO + col0 + 8 * c) = v;
   }
-  if (lse && hi == 0 && row0 + l32 < p.N)
-    p.lse[(size_t)bh * p.N + row0 + l32] = live ? m * p.scale_eff + logf(lt) : -INFINITY;
+  if (lse) {
+    // l_lse >= 0: the log-sum-exp takes that (lane-partial) sum instead of l
+    const float ll = l_lse >= 0.0f ? sum_halves(l_lse) : lt;
+    if (hi == 0 && row0 + l32 < p.N)
+      p.lse[(size_t)bh * p.N + row0 + l32] = live ? m * p.scale_eff + logf(ll) : -INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1397,6 +1403,373 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// fp8 e4m3 kernel, software-pipelined: both products on the fp8 matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4), S^T = K Q^T per 32-key half and
+// O^T += V^T P^T per 64-key tile (FlashAttention (ES), "FlashAttention-3
+// (2024)", names FP8 for the whole fused kernel).
+//
+// The same workgroup shape, causal folding, XCD-aware order and lazy
+// reference maximum as the 16-bit pipelined kernel; what differs:
+//   * K and V tiles are both fp8 and both reach LDS through direct-to-LDS
+//     copies. The V^T operand of a P V product (one head dimension, 32
+//     consecutive keys per lane) comes from four transposing byte reads
+//     (ds_read_b64_tr_b8): in each 16-lane group, lane 2j+h addresses key j,
+//     head dims 8h..8h+7, and lane i receives head dim i of the 8 keys.
+//   * P is rounded to e4m3 as P' = P * 2^4 (the 4 folded into the exponent
+//     bias; the product's E8M0 scale 2^-4 undoes it exactly), so P down to
+//     2^-10 keeps e4m3's normal precision. The row sum l adds the same rounded
+//     P' that multiply V, on the matrix cores: one 16x16x128 product per tile
+//     of an e4m3 0/1 matrix with the tile's P^T operand, whose rows 0 and 4
+//     select the lane groups of each query, so that the first accumulator
+//     register of lane l < 32 is row l's sum (and 0 in lanes 32-63).
+//   * The products take a whole tile's P (K = 64 keys), but each lane holds 16
+//     keys of each half; one v_permlane32_swap per 4 keys trades halves with
+//     lane l^32, after which lane (q, h) holds the 32 keys of half h of query
+//     q in order, as the B operand wants.
+//   * P of a tile's first half is formed one block before the product; if the
+//     second half then moves the row's reference maximum, the move is a whole
+//     number n of powers of two and the pending first half's e4m3 values are
+//     scaled by 2^-n in place (exact unless they fall below e4m3's normal
+//     range; l sums the re-rounded values, as V is multiplied by them).
+//
+// Per iteration t (K of tile t+1 in kb, V of tile t in vb), block A: the S
+// products of tile t+1 with the softmax of tile t's second half; block B:
+// the P V products of tile t with the softmax of tile t+1's first half.
+// Three score buffers rotate: s1 (tile t, second half), x (tile t+1, first
+// half, consumed in block B) and y (tile t+1, second half, next s1).
+// ---------------------------------------------------------------------------
+
+// v8_swz: fp8 V rows (D bytes): the 16 rows x 2 slots one transposing read
+// touches per 32 lanes land on distinct banks.
+template <int D>
+__device__ __forceinline__ int v8_swz(int r) {
+  if constexpr (D == 128) return ((r >> 1) & 3) << 1;
+  return ((r >> 2) & 1) << 1;
+}
+
+constexpr int kP8Shift = 4;          // P' = P * 2^4 before rounding to e4m3
+constexpr float kP8Bound = 420.0f;  // a lane's half sum of P' above this: rescale
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
+  using T = __bf16;  // O
+  constexpr int BR = NW * 32;   // query rows per workgroup
+  constexpr int BC = 64;        // keys per LDS tile
+  constexpr int KS = D / 64;    // S MFMA steps over the head dim per half
+  constexpr int DB = D / 32;    // 32-wide blocks of O^T (P V products per tile)
+  constexpr int TB = BC * D;    // bytes per K or V tile
+  constexpr int CPR = D / 16;   // 16-byte slots per row
+  constexpr int NC = TB / 1024;  // 1 KB copies per tile
+  constexpr int ND = (NC + NW - 1) / NW;  // copies per wave per tile (some idle)
+  constexpr int LA = FA_PIPE_LOOKAHEAD;
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1s[TB];
+  // (the staging array's smaller alignment places it after the tiles, whose
+  // addresses then fit the LDS instructions' 16-bit offsets)
+  __shared__ __attribute__((aligned(16))) unsigned char ostage[NW * 32 * D * 2];
+  auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? k0s : k1s; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? v0s : v1s; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // Work unit u of head bh, causal query tiles folded in pairs, as in
+  // attn_fwd_pipe.
+  const int units = CAUSAL ? (p.n_qt + 1) / 2 : p.n_qt;
+  int bh, u;
+  {
+    const int bid = blockIdx.x, total = gridDim.x;
+    int logical = bid;
+    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+    bh = logical / units;
+    u = logical - bh * units;
+  }
+  const int n_qt = p.n_qt;
+  const int N = p.N;
+
+  // Q^T operand: lane holds its query row's head dims [64*st + 32*hi, +32).
+  i32x8 qf[KS];
+
+  auto process = [&](int qt) __attribute__((always_inline)) {
+  const int ln = pinned_int(lane);
+  int koff[2 * KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      koff[2 * st + x] = (ln & 31) * D + (((4 * st + 2 * (ln >> 5) + x) ^ k8_swz<D>(ln & 31)) << 4);
+  // V^T operand of P V block db, read q at voff[db] + 8 * q * D: key row
+  // 32*(group/2) + 8q + (i/2), head dims 32db + 16*(group%2) + 8*(i%2) + [0, 8).
+  int voff[DB];
+  {
+    const int g = (ln >> 4) & 3, i = ln & 15;
+    const int r = 32 * (g >> 1) + (i >> 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      voff[db] = r * D + (((2 * db + (g & 1)) ^ v8_swz<D>(r)) << 4) + 8 * (i & 1);
+  }
+  const RowRange rr = row_range_at<BR, BC, CAUSAL>(p, bh, qt, wave, l32);
+  const size_t kv_head = (size_t)rr.kv_bh * N * D;  // bytes
+  {
+    const auto rq = tile_rsrc((const unsigned char*)p.q + (size_t)rr.bh * N * D, rr.q_wg0 / BR, BR, N, D);
+    const int row = rr.qrow - rr.q_wg0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int off = row * D + 64 * s + 32 * hi;
+      qf[s] = __builtin_shufflevector(load16(rq, off), load16(rq, off + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+  const auto rsK = buffer_rsrc((const unsigned char*)p.k + kv_head, rr.kl * D);
+  const auto rsV = buffer_rsrc((const unsigned char*)p.v + kv_head, rr.kl * D);
+  // Tile j of K or V straight into LDS, 16-byte slots permuted per row.
+  auto copy_tile = [&](int j, unsigned char* dst, auto is_v) __attribute__((always_inline)) {
+    constexpr bool IV = decltype(is_v)::value;
+#pragma unroll
+    for (int cc = 0; cc < ND; ++cc) {
+      const int blk = cc * NW + wave;
+      if (NC % NW == 0 || blk < NC) {
+        const int slot = blk * 64 + lane;
+        const int r = slot / CPR, ps = slot % CPR;
+        const int lc = ps ^ (IV ? v8_swz<D>(r) : k8_swz<D>(r));
+        lds_copy16(IV ? rsV : rsK, dst + blk * 1024, j * TB + r * D + (lc << 4));
+      }
+    }
+  };
+  // S^T = K Q^T over keys [32h, 32h + 32) of the K tile at kb
+  auto scores = [&](const unsigned char* kb, int h, f32x16& s) __attribute__((always_inline)) {
+    s = f32x16{};
+    i32x8 ring[LA + 1];
+#pragma unroll
+    for (int t = 0; t < KS + LA; ++t) {
+      if (t < KS) {
+        const unsigned char* b = kb + 32 * h * D;
+        ring[t % (LA + 1)] = __builtin_shufflevector(*(const i32x4*)(b + koff[2 * t]),
+                                                     *(const i32x4*)(b + koff[2 * t + 1]),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const int v = t - LA;
+      if (v >= 0)  // formats 0/0: fp8 e4m3 operands; E8M0 scales 127 = 1.0
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[v % (LA + 1)], qf[v], s, 0, 0, 0,
+                                                            127, 0, 127);
+    }
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  // base = -m * c + kP8Shift (+inf while m = -inf): P' = exp2(c * s + base).
+  // ls[0] sums the rounded P (the weights V is multiplied by, so O is their
+  // normalised combination); lx sums the unrounded P' for the log-sum-exp.
+  float m = -INFINITY, base = INFINITY, lx = 0.0f;
+  f32x4 ls = {};
+  const float c = p.c;
+  // e4m3 A operand of the row-sum product (the format of the P^T operand, so
+  // that both spread the K dimension over the lanes alike): lane (row r =
+  // lane % 16, group g = lane / 16) holds 1.0 (code 0x38) in row 0 for groups
+  // 0 and 2 and in row 4 for groups 1 and 3, else 0. The P^T operand's lane
+  // group g holds query l % 32 of its lanes: groups 0 and 2 queries 0-15,
+  // groups 1 and 3 queries 16-31. Output row 0 (lanes 0-15) is then the sum
+  // of queries 0-15, row 4 (lanes 16-31) of queries 16-31, and lanes 32-63
+  // hold 0, so summing lanes l and l^32 gives each row's sum once.
+  i32x8 sel_a{};
+  {
+    const int r = lane & 15, g = lane >> 4;
+    const int w = (r == 0 && (g & 1) == 0) || (r == 4 && (g & 1) == 1) ? 0x38383838 : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sel_a[i] = w;
+  }
+
+  // P' of one half (16 scores of this lane's row) against `b`, rounded to
+  // e4m3 into 4 words; rx gets the sum of the unrounded values.
+  auto round_half = [&](const f32x16& s, float b, i32x4& pw, float& rx) __attribute__((always_inline)) {
+    rx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = fast_exp2(fmaf(s[4 * w + e], c, b));
+      // (the first conversion's other half is overwritten by the second)
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __builtin_bit_cast(int, x[2]), false);
+      d = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], d, true);
+      pw[w] = d;
+      rx += (x[0] + x[1]) + (x[2] + x[3]);
+    }
+  };
+  auto half_max = [&](const f32x16& s) __attribute__((always_inline)) {
+    float x = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) x = fmaxf(x, s[i]);
+    return max_halves(x);
+  };
+  // The 4 e4m3 words of a pending half scaled by 2^-n (n >= 0).
+  auto rescale_half = [&](i32x4& pw, int n) __attribute__((always_inline)) {
+    const float sc = __builtin_ldexpf(1.0f, -n);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(pw[w], false);
+      const f32x2 up = __builtin_amdgcn_cvt_pk_f32_fp8(pw[w], true);
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0] * sc, lo[1] * sc, pw[w], false);
+      pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(up[0] * sc, up[1] * sc, d, true);
+    }
+  };
+  // P' of a half with the reference check. Without a pending half the rare
+  // branch moves the reference to the row maximum; with one (pend, the P' of
+  // the tile's first half, not yet multiplied) it moves it up by a whole
+  // number n of powers of two and scales pend by 2^-n.
+  auto probs = [&](f32x16& s, i32x4& pw, int k0, auto masked, auto pending, i32x4& pend)
+      __attribute__((always_inline)) {
+    if constexpr (FA_PIPE_IGLP >= 0) __builtin_amdgcn_iglp_opt(FA_PIPE_IGLP);
+    if constexpr (decltype(masked)::value) {
+      auto& s1 = *reinterpret_cast<f32x16(*)[1]>(&s);
+      apply_mask<1, CAUSAL>(s1, k0, rr.kl, rr.qrow, hi);
+    }
+    float rx;
+    round_half(s, base, pw, rx);
+    if (__builtin_amdgcn_ballot_w64(!(rx <= kP8Bound)) != 0) {
+      const float mx = half_max(s);
+      float alpha;
+      if (decltype(pending)::value && m != -INFINITY) {
+        // up by whole powers of two: the reference stays exactly base - steps
+        const float steps = fmaxf(0.0f, ceilf((mx - m) * c));
+        const int n = (int)fminf(steps, 126.0f);
+        alpha = pinned(__builtin_ldexpf(1.0f, -n));
+        m += steps / c;
+        base -= steps;
+        rescale_half(pend, n);
+      } else {
+        const float mn = fmaxf(m, mx);
+        alpha = pinned(mn == m ? 1.0f : fast_exp2((m - mn) * c));  // exp2(-inf) = 0
+        m = mn;
+        base = fmaf(-mn, c, (float)kP8Shift);  // +inf while the row has no key
+      }
+      lx *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ls[i] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      round_half(s, m == -INFINITY ? 0.0f : base, pw, rx);
+    }
+    lx += rx;
+  };
+  // O^T += V^T P^T over the tile in vb: p0, p1 the rounded P' of its halves.
+  auto pv = [&](const unsigned char* vb, const i32x4& p0, const i32x4& p1)
+      __attribute__((always_inline)) {
+    i32x8 b;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x2 r = __builtin_amdgcn_permlane32_swap((unsigned)p0[w], (unsigned)p1[w], false, false);
+      b[2 * w] = (int)r[0];
+      b[2 * w + 1] = (int)r[1];
+    }
+    constexpr int sb = 127 - kP8Shift;  // E8M0 2^-4 undoes P' = P * 2^4
+    // row sums (formats 0/0: e4m3 A and B)
+    ls = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel_a, b, ls, 0, 0, 0, 127, 0, sb);
+    i32x8 ring[LA + 1];
+#pragma unroll
+    for (int t = 0; t < DB + LA; ++t) {
+      if (t < DB) {
+        const unsigned char* a = vb + voff[t];
+        i32x8 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const auto rq = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2*)(a + 8 * q * D));
+          v[2 * q] = rq[0];
+          v[2 * q + 1] = rq[1];
+        }
+        ring[t % (LA + 1)] = v;
+      }
+      const int v = t - LA;
+      if (v >= 0)
+        o[v] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[v % (LA + 1)], b, o[v], 0, 0, 0,
+                                                               127, 0, sb);
+    }
+  };
+
+  f32x16 sA, sB, sC;
+  i32x4 p0, p1;
+  // One iteration with score buffers s1 (tile t, second half), x, y (tile
+  // t+1): block A, then block B.
+  auto iteration = [&](int t, const unsigned char* kb, const unsigned char* vb, f32x16& s1,
+                       f32x16& x, f32x16& y, auto has_next, auto mask_a, auto mask_b)
+      __attribute__((always_inline)) {
+    constexpr bool HN = decltype(has_next)::value;
+    if constexpr (HN) {
+      scores(kb, 0, x);
+      scores(kb, 1, y);
+    }
+    probs(s1, p1, BC * t + 32, mask_a, std::true_type{}, p0);
+    pv(vb, p0, p1);
+    if constexpr (HN) probs(x, p0, BC * (t + 1), mask_b, std::false_type{}, p1);
+  };
+  auto copies = [&](int t, unsigned char* kx, unsigned char* vx) __attribute__((always_inline)) {
+    copy_tile(t + 2, kx, std::false_type{});
+    copy_tile(t + 1, vx, std::true_type{});
+  };
+  auto sync_after = [&]() __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();
+  };
+
+  copy_tile(0, k0s, std::false_type{});
+  copy_tile(1, k1s, std::false_type{});
+  copy_tile(0, v0s, std::true_type{});
+  wait_vmem();
+  __syncthreads();
+  if (rr.wnt > 0) {
+    scores(k0s, 0, sB);
+    scores(k0s, 1, sA);
+    if (0 < rr.wfull) probs(sB, p0, 0, std::false_type{}, std::false_type{}, p1);
+    else probs(sB, p0, 0, std::true_type{}, std::false_type{}, p1);
+  }
+  __syncthreads();  // K of tile 0 is read by every wave before its buffer is refilled
+  // Iterations [0, ts): unmasked with a next tile, two per pass (the K/V
+  // buffers alternate, and so do the roles of sA and sC); then the rest one
+  // at a time with sA as s1, sC moved into sA after each.
+  const int ts = max(0, rr.wfull - 1);
+  int t = 0;
+  for (; t + 2 <= ts; t += 2) {
+    copies(t, k0s, v1s);
+    iteration(t, k1s, v0s, sA, sB, sC, std::true_type{}, std::false_type{}, std::false_type{});
+    sync_after();
+    copies(t + 1, k1s, v0s);
+    iteration(t + 1, k0s, v1s, sC, sB, sA, std::true_type{}, std::false_type{}, std::false_type{});
+    sync_after();
+  }
+  for (; t < rr.nt; ++t) {
+    const int q = t & 1;
+    copies(t, kbuf(q), vbuf(q ^ 1));
+    if (t < rr.wnt) {
+      if (t + 1 < rr.wfull)
+        iteration(t, kbuf(q ^ 1), vbuf(q), sA, sB, sC, std::true_type{}, std::false_type{}, std::false_type{});
+      else if (t + 1 < rr.wnt)
+        iteration(t, kbuf(q ^ 1), vbuf(q), sA, sB, sC, std::true_type{}, std::true_type{}, std::true_type{});
+      else
+        iteration(t, kbuf(q ^ 1), vbuf(q), sA, sB, sC, std::false_type{}, std::true_type{}, std::false_type{});
+      sA = sC;
+    }
+    sync_after();
+  }
+  // O / l through this wave's own staging slice (K/V buffers stay free);
+  // LSE from the unrounded sum
+  epilogue_staged<T, D, DB>(p, rr.bh, rr.qw0, lane, (kP8Shift - base) / c, ls[0], o,
+                            ostage + wave * (32 * D * 2), 0, true,
+                            lx * (1.0f / (1 << kP8Shift)));
+  __syncthreads();  // every wave is past the K/V buffers before the next item's copies
+  };
+
+  const int items = CAUSAL && u != n_qt - 1 - u ? 2 : 1;
+#pragma nounroll
+  for (int it = 0; it < items; ++it) process(CAUSAL && it == 0 ? n_qt - 1 - u : u);
+}
+
+// ---------------------------------------------------------------------------
 // fp8 e4m3 kernel: S^T on the fp8 matrix cores (32x32x64), P V in bf16.
 // V's fp8 codes are widened to bf16 exactly when staged into LDS (every e4m3
 // value is a bf16 value), and P is rounded to bf16 as in the bf16 kernel.
@@ -2256,6 +2629,8 @@ hipError_t launch_d(Kind kind, const Params& p, hipStream_t s) {
         return launch(attn_fwd_pipe<Bf16, D, FA_WIDE_WAVES, C, true>, p, FA_WIDE_WAVES * 64, s,
                       pipe_units(p, C));
       return launch(attn_fwd_fp8<D, kWaves, FA_KEY_TILE, C>, p, T, s);
+    case Kind::FP8_P8:  // every shape: one kernel, one rounding of P
+      return launch(attn_fwd_pipe8<D, FA_WIDE_WAVES, C>, p, FA_WIDE_WAVES * 64, s, pipe_units(p, C));
     case Kind::F32: return launch(attn_fwd_f32<D, kWaves, 32, C>, p, T, s);
   }
   return hipErrorInvalidValue;
@@ -2273,6 +2648,7 @@ int rows_per_block(Kind kind, int d, int N, bool causal, bool window) {
   if (kind == Kind::BF16 || kind == Kind::F16)
     return use_pipe(N, causal) ? FA_WIDE_WAVES * 32 : FA_DMA_WAVES * 32;
   if (kind == Kind::FP8 && use_pipe(N, causal)) return FA_WIDE_WAVES * 32;
+  if (kind == Kind::FP8_P8) return FA_WIDE_WAVES * 32;
   return kWaves * 32;
 }
 

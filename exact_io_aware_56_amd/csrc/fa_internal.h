@@ -70,7 +70,9 @@ struct BwdParams {
   float scale;
 };
 
-enum class Kind { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
+// FP8_P8: fp8 inputs with P rounded to e4m3 for the P V product (not a
+// public dtype value; fa_fwd_fp8_p8 selects it).
+enum class Kind { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3, FP8_P8 = 4 };
 
 // Rows of Q owned by one workgroup for a problem's kind, d, N and mask; 0 if
 // d is unsupported. Must agree with the kernel launch_forward picks.

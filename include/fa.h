@@ -48,8 +48,8 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd; 5: fa_fwd_window;
-                             6: fa_fwd_varlen; 7: fa_fwd_decode_noalloc */
+#define FA_ABI_VERSION 8  /* 2: fa_fwd_gqa; 3: fa_fwd_decode; 4: fa_bwd; 5: fa_fwd_window;
+                             6: fa_fwd_varlen; 7: fa_fwd_decode_noalloc; 8: fa_fwd_fp8_p8 */
 
 typedef enum {
   FA_DTYPE_FP32 = 0,     /* float32 in, float32 out                          */
@@ -95,12 +95,14 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            const int32_t* key_len, int dtype, void* stream);
 
 /*
- * fa_fwd_fp8 -- fa_fwd for fp8 e4m3 inputs quantised per tensor.
+ * fa_fwd_fp8 -- fa_fwd for fp8 e4m3 inputs quantised per tensor (the FP8
+ * support of FlashAttention (ES), "FlashAttention-3 (2024)").
  *
  * The stored codes Q8, K8, V8 represent Q = q_descale * Q8, K = k_descale *
  * K8 and V = v_descale * V8. The logits are scale * q_descale * k_descale *
- * (Q8 K8^T); O = v_descale * softmax(...) V8, written as bfloat16. Both
- * matrix products accumulate in fp32. The descales must be finite and > 0.
+ * (Q8 K8^T); O = v_descale * softmax(...) V8, written as bfloat16. S = Q K^T
+ * runs on the fp8 matrix cores; P stays in bfloat16 for the P V product.
+ * Both products accumulate in fp32. The descales must be finite and > 0.
  * fa_fwd(..., FA_DTYPE_FP8_E4M3, ...) equals this call with descales 1.0.
  * Arguments otherwise as fa_fwd.
  */
@@ -108,6 +110,26 @@ int fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, void* O_bf16, flo
                int B, int H, int N, int d, float scale, int causal,
                const int32_t* key_len, float q_descale, float k_descale,
                float v_descale, void* stream);
+
+/*
+ * fa_fwd_fp8_p8 -- fa_fwd_fp8 with both products on the fp8 matrix cores:
+ * P is rounded to e4m3 for the P V product, as in the FP8 form of
+ * FlashAttention (ES), "FlashAttention-3 (2024)" (FP8 operands, fp32
+ * accumulation).
+ *
+ * Arguments, layouts, ownership and status codes as fa_fwd_fp8 (d 64 or
+ * 128). The row sum l adds the same rounded P that multiply V, so O is still
+ * a convex combination of V's rows; its weights carry e4m3's rounding (3
+ * mantissa bits, at most 2^-4 relative per weight), so a row's error is at
+ * most about 2 * 2^-4 * sum_j w_j |v_j - O| per column: small where the
+ * weights spread over many keys (the long fp8 workload stays within 5e-2 of
+ * the exact result), up to ~0.1 where two or three keys with different V
+ * rows share a row's weight. LSE is computed from the unrounded P.
+ */
+int fa_fwd_fp8_p8(const void* Q8, const void* K8, const void* V8, void* O_bf16, float* LSE,
+                  int B, int H, int N, int d, float scale, int causal,
+                  const int32_t* key_len, float q_descale, float k_descale,
+                  float v_descale, void* stream);
 
 /*
  * fa_fwd_gqa -- fa_fwd with K/V heads shared by groups of query heads

@@ -33,11 +33,12 @@ def to_device(w):
     return q, k, v, kl
 
 
-def run(w, stream=None):
-    """Run the library on workload w; returns (O, LSE) as float64 numpy arrays."""
+def run(w, stream=None, p8=False):
+    """Run the library on workload w (p8: fp8 inputs through fa_fwd_fp8_p8);
+    returns (O, LSE) as float64 numpy arrays."""
     q, k, v, kl = to_device(w)
     o, lse = fa.fwd(q, k, v, scale=w.spec.scale, causal=w.spec.causal, key_len=kl,
-                    descale=w.descale, stream=stream)
+                    descale=w.descale, stream=stream, p8=p8)
     torch.cuda.synchronize()
     return o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
 

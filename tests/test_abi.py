@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 7
+    assert lib.fa_abi_version() == 8
     assert _lib.status_name(0) == "FA_OK"
     assert _lib.status_name(-1) == "FA_ERR_INVALID_ARG"
     assert _lib.status_name(-2) == "FA_ERR_UNSUPPORTED"
@@ -70,15 +70,26 @@ def test_invalid_arguments_are_rejected_on_host(kw, status):
     assert _lib.load().fa_last_error().decode() != ""
 
 
-def test_fp8_descales_are_validated():
+@pytest.mark.parametrize("entry", ["fa_fwd_fp8_raw", "fa_fwd_fp8_p8_raw"])
+def test_fp8_descales_are_validated(entry):
+    f = getattr(_lib, entry)
     for bad in (0.0, -2.0, math.inf, math.nan):
-        st = _lib.fa_fwd_fp8_raw(P, P, P, P, P, 1, 1, 16, 128, 0.1, 1, None, bad, 1.0, 1.0, None)
-        assert st == -1
-        st = _lib.fa_fwd_fp8_raw(P, P, P, P, P, 1, 1, 16, 128, 0.1, 1, None, 1.0, 1.0, bad, None)
-        assert st == -1
+        assert f(P, P, P, P, P, 1, 1, 16, 128, 0.1, 1, None, bad, 1.0, 1.0, None) == -1
+        assert f(P, P, P, P, P, 1, 1, 16, 128, 0.1, 1, None, 1.0, 1.0, bad, None) == -1
     # scale * q_descale * k_descale must stay finite
-    st = _lib.fa_fwd_fp8_raw(P, P, P, P, P, 1, 1, 16, 128, 3e38, 1, None, 1e10, 1.0, 1.0, None)
-    assert st == -1
+    assert f(P, P, P, P, P, 1, 1, 16, 128, 3e38, 1, None, 1e10, 1.0, 1.0, None) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(d=256), -2), (dict(d=96), -2), (dict(d=32), -2), (dict(q=None), -1), (dict(N=0), -1),
+    (dict(o=P + 4), -1), (dict(scale=math.nan), -1),
+])
+def test_fp8_p8_entry_point_rejects_bad_arguments(args, status):
+    a = dict(q=P, N=16, d=128, scale=0.1, o=P)
+    a.update(args)
+    st = _lib.fa_fwd_fp8_p8_raw(a["q"], P, P, a["o"], P, 1, 1, a["N"], a["d"], a["scale"], 1, None,
+                                1.0, 1.0, 1.0, None)
+    assert st == status
 
 
 def gqa_call(**kw):
@@ -206,12 +217,18 @@ def test_varlen_entry_point_rejects_bad_arguments(kw, status):
     assert _lib.load().fa_last_error().decode() != ""
 
 
+def sig_default(fn, name):
+    import inspect
+    return inspect.signature(fn).parameters[name].default
+
+
 def test_python_binding_names_the_entry_points():
     import inspect
 
     import exact_io_aware_56_amd as fa
 
     assert callable(fa.fa_fwd) and callable(fa.fa_fwd_fp8) and callable(fa.fa_fwd_gqa)
+    assert callable(fa.fa_fwd_fp8_p8) and sig_default(fa.fwd, "p8") is False
     sig = inspect.signature(fa.fwd)
     assert list(sig.parameters)[:3] == ["q", "k", "v"]
     for name in ("scale", "causal", "key_len"):

@@ -19,12 +19,15 @@ from parity import TOL, every_element_errors, run, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["long_causal_bf16", "long_causal_fp8"])
-def test_long_workload_every_element(name):
+@pytest.mark.parametrize("name,p8", [("long_causal_bf16", False), ("long_causal_fp8", False),
+                                     ("long_causal_fp8", True)])
+def test_long_workload_every_element(name, p8):
+    """p8: the fp8 workload through fa_fwd_fp8_p8 (P rounded to e4m3 for P V),
+    held to the same fp8 bounds."""
     w = W.draw(W.SPECS[name])
     s = w.spec
-    say(f"case {name} every element B{s.B} H{s.H} N{s.N} d{s.d} {s.dtype} seed={s.seed}")
-    o, lse = run(w)
+    say(f"case {name} every element B{s.B} H{s.H} N{s.N} d{s.d} {s.dtype} p8={p8} seed={s.seed}")
+    o, lse = run(w, p8=p8)
     assert np.all(np.isfinite(o)), "non-finite O"
     t0 = time.perf_counter()
     mx, mean, dl, same_inf = every_element_errors(w, o, lse)
