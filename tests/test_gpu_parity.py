@@ -7,6 +7,7 @@ against the full oracle where it finishes in seconds and against oracle rows
 computed one by one otherwise.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -161,7 +162,9 @@ def test_named_workload_full_oracle(name):
     w = W.draw(W.SPECS[name])
     say(f"case {name} full oracle seed={w.spec.seed}")
     o, lse = run(w)
+    t0 = time.perf_counter()
     o_ref, lse_ref = full_oracle(w)
+    say(f"  {name}: oracle {time.perf_counter() - t0:.2f} s")
     assert_close(o, lse, o_ref, lse_ref, w.spec.dtype, name)
 
 
