@@ -701,10 +701,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_d256(Params p) {
 // ---------------------------------------------------------------------------
 
 // Slot permutations (16-byte slots, row = D*2 bytes). k_swz keeps the 16 rows
-// read by one half-wave at one logical slot on 16 different slots; v_swz
-// keeps the 8 rows x 64 bytes of one transposing read on distinct banks.
+// a quarter-wave reads at one logical slot on 16 distinct 16-byte bank
+// groups: with 256-byte or longer rows every row starts at bank 0, so the
+// slots themselves must differ (r mod D/8); with 128-byte rows (d = 64) odd
+// rows start half-way round the banks, so rows r and r ^ 1 may share a slot
+// and the permutation takes r / 2. v_swz keeps the 8 rows x 64 bytes of one
+// transposing read on distinct banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
+  if constexpr (D == 64) return (r >> 1) & 7;
   return r & (D / 8 - 1);
 }
 // fp8 K rows (D bytes, D/16 slots): the 16 rows a quarter-wave reads at one
