@@ -2421,29 +2421,38 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   copies(1, 1);
   wait_vmem_keep<2 * NCPW>();  // tile 0 landed (tile 1 may be in flight)
   __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    const int buf = j % kBwdBufs;
-    copies(j + 2, (j + 2) % kBwdBufs);  // past the end: empty ranges, nothing moves
-    auto tile = [&](auto masked) __attribute__((always_inline)) {
-      f32x16 s[1] = {f32x16{}};
-      f32x16 dp = {};
-      two_products<E, D>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
-      if constexpr (decltype(masked)::value) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
-      v8 ds[2];
+  // Key tile j (buffer j % 3, a compile-time index: the loop is unrolled over
+  // the three buffers, so every LDS address is a lane offset plus an
+  // immediate). One body serves every tile; the mask is applied in place only
+  // on the wave's diagonal or ragged tiles (j >= wfull, a wave-uniform test).
+  auto tile = [&](int j, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    f32x16 s[1] = {f32x16{}};
+    f32x16 dp = {};
+    two_products<E, D>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
+    if (j >= wfull) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
+    v8 ds[2];
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps)
+    for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * ps + e;
-          const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
-          ds[ps][e] = E::cvt(pr * (dp[i] - dl));
-        }
-      tr_product<E, D>(kb[buf], sz, ds, dq);
-    };
-    if (j < wfull) tile(std::false_type{});
-    else if (j < wnt) tile(std::true_type{});
-    wait_vmem_keep<2 * NCPW>();  // tile j+1 landed; tile j+2 may be in flight
-    __syncthreads();
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * ps + e;
+        const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
+        ds[ps][e] = E::cvt(pr * (dp[i] - dl));
+      }
+    tr_product<E, D>(kb[buf], sz, ds, dq);
+  };
+  for (int j0 = 0; j0 < nt; j0 += kBwdBufs) {
+    static_for<kBwdBufs>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      const int j = j0 + q;
+      if (j < nt) {  // workgroup-uniform: the barrier below is reached by every wave
+        copies(j + 2, (q + 2) % kBwdBufs);  // past the end: empty ranges, nothing moves
+        if (j < wnt) tile(j, qc);
+        wait_vmem_keep<2 * NCPW>();  // tile j+1 landed; tile j+2 may be in flight
+        __syncthreads();
+      }
+    });
   }
   wait_vmem();
   if (row_ok) store_grad<T, DB>((T*)p.dq + head + (size_t)qrow * D, hi, p.scale, dq);
@@ -2535,16 +2544,29 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     if (tid < 32) ls[0][tid] = lreg, dls[0][tid] = dlreg;
   }
   __syncthreads();
-  for (int u = 0; u < n_iter; ++u) {
-    const int buf = u % kBwdBufs, nbuf = (u + 1) % kBwdBufs;
+  // Iteration u uses buffer u % 3, a compile-time index (the loop is unrolled
+  // over the three buffers). Masks: only the wave's diagonal query tile (some
+  // key above some query row) and a ragged last key block (keys at or past
+  // kl) need one; there the masked scores are set to -inf in place before
+  // the exponentials, elsewhere the scores go straight through.
+  auto iter = [&](int u, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value, nbuf = (buf + 1) % kBwdBufs;
     int t, lim;
     size_t qhead;
     tile_of(u, t, qhead, lim);
     row_stats(u + 1);
-    copies(u + 2, (u + 2) % kBwdBufs);
+    copies(u + 2, (buf + 2) % kBwdBufs);
     if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
       f32x16 s = {}, dp = {};
       two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
+      if ((CAUSAL && 32 * t < kw0 + 31) || kw0 + 32 > kl) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qry = 32 * t + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const bool ok = key < kl && (!CAUSAL || key <= qry);
+          s[i] = ok ? s[i] : -INFINITY;
+        }
+      }
       v8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -2553,9 +2575,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q4 + e;
-          const int qry = 32 * t + 8 * q4 + 4 * hi + e;
-          const bool ok = key < kl && (!CAUSAL || key <= qry);
-          const float pr = ok ? fast_exp2(fmaf(s[i], c, -l4[e])) : 0.0f;
+          const float pr = fast_exp2(fmaf(s[i], c, -l4[e]));
           pf[i >> 3][i & 7] = E::cvt(pr);
           dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
         }
@@ -2566,6 +2586,11 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     wait_vmem_keep<2 * NCPW>();  // row stats u+1 and tile u+1 landed; tile u+2 may be in flight
     if (tid < 32) ls[nbuf][tid] = lreg, dls[nbuf][tid] = dlreg;
     __syncthreads();
+  };
+  for (int u0 = 0; u0 < n_iter; u0 += kBwdBufs) {
+    static_for<kBwdBufs>([&](auto qc) __attribute__((always_inline)) {
+      if (u0 + decltype(qc)::value < n_iter) iter(u0 + decltype(qc)::value, qc);  // workgroup-uniform
+    });
   }
   wait_vmem();
   if (key < N) {
