@@ -2362,8 +2362,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   using v8 = typename E::v8;
   constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
   constexpr int NCPW = TB / 1024 / kBwdWaves;  // copies per wave per tile and tensor
-  __shared__ __attribute__((aligned(1024))) unsigned char kb[kBwdBufs][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char vb[kBwdBufs][TB];
+  constexpr int NB = 4;  // K / V buffers: tile j + 3 is copied while j and j + 1 are read
+  __shared__ __attribute__((aligned(1024))) unsigned char kb[NB][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb[NB][TB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2419,18 +2420,29 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
   copies(0, 0);
   copies(1, 1);
-  wait_vmem_keep<2 * NCPW>();  // tile 0 landed (tile 1 may be in flight)
+  copies(2, 2);
+  wait_vmem_keep<2 * NCPW>();  // tiles 0 and 1 landed (tile 2 may be in flight)
   __syncthreads();
-  // Key tile j (buffer j % 3, a compile-time index: the loop is unrolled over
-  // the three buffers, so every LDS address is a lane offset plus an
-  // immediate). One body serves every tile; the mask is applied in place only
-  // on the wave's diagonal or ragged tiles (j >= wfull, a wave-uniform test).
+  // Software pipeline over the key tiles: iteration j issues the S and dP
+  // products of tile j + 1 in the same basic block as the softmax of tile j
+  // and its dQ product, so the matrix cores have work while the vector ALU
+  // forms dS. Tile j + 1's products are computed even where this wave will
+  // not use them (past its last tile, or past nt): they only read LDS, and
+  // their results are dropped. Tiles this wave does not need (j >= wnt) are
+  // fully masked (the causal bound or key_len), so they add exact zeros to dQ.
+  // The loop is unrolled over the four buffers: buffer indices and LDS
+  // addresses are compile-time, and the S / dP registers of consecutive tiles
+  // alternate between two sets (sp[j % 2], dpp[j % 2]) with no copies.
+  f32x16 sp[2][1] = {{f32x16{}}, {f32x16{}}}, dpp[2] = {f32x16{}, f32x16{}};
+  two_products<E, D>(kb[0], vb[0], sz, hi, qf, df, sp[0][0], dpp[0]);
   auto tile = [&](int j, auto bufc) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value;
-    f32x16 s[1] = {f32x16{}};
-    f32x16 dp = {};
-    two_products<E, D>(kb[buf], vb[buf], sz, hi, qf, df, s[0], dp);
+    constexpr int buf = decltype(bufc)::value, nb1 = (buf + 1) % NB, x = buf & 1;
+    f32x16 (&s)[1] = sp[x];
+    const f32x16& dp = dpp[x];
     if (j >= wfull) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
+    sp[x ^ 1][0] = f32x16{};
+    dpp[x ^ 1] = f32x16{};
+    two_products<E, D>(kb[nb1], vb[nb1], sz, hi, qf, df, sp[x ^ 1][0], dpp[x ^ 1]);
     v8 ds[2];
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps)
@@ -2442,14 +2454,14 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
       }
     tr_product<E, D>(kb[buf], sz, ds, dq);
   };
-  for (int j0 = 0; j0 < nt; j0 += kBwdBufs) {
-    static_for<kBwdBufs>([&](auto qc) __attribute__((always_inline)) {
+  for (int j0 = 0; j0 < nt; j0 += NB) {
+    static_for<NB>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
       const int j = j0 + q;
       if (j < nt) {  // workgroup-uniform: the barrier below is reached by every wave
-        copies(j + 2, (q + 2) % kBwdBufs);  // past the end: empty ranges, nothing moves
+        copies(j + 3, (q + 3) % NB);  // past the end: empty ranges, nothing moves
         if (j < wnt) tile(j, qc);
-        wait_vmem_keep<2 * NCPW>();  // tile j+1 landed; tile j+2 may be in flight
+        wait_vmem_keep<2 * NCPW>();  // tile j+2 landed; tile j+3 may be in flight
         __syncthreads();
       }
     });
@@ -2506,40 +2518,49 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   sz.init(pinned_int(lane));
 
   // iteration u: query head g*group + u / per_head, query tile t_begin + u % per_head
-  auto tile_of = [&](int u, int& t, size_t& qhead, int& lim) __attribute__((always_inline)) {
-    const int ph = max(per_head, 1);
-    const int hq = g * p.group + min(u / ph, p.group - 1);
-    t = t_begin + u % ph;
-    qhead = ((size_t)b * p.H + hq) * N;
-    lim = u < n_iter ? N : 0;
+  // Cursor of iteration u: query tile t and query head hq (index within the
+  // group) of a scan that runs over t in [t_begin, t_begin + per_head) for each
+  // head of the group in turn; advanced by one per iteration (no division in
+  // the loop). Past n_iter the head index is clamped and the row limit is 0.
+  struct Cur {
+    int u, t, hq;
   };
-  auto copies = [&](int u, int buf) __attribute__((always_inline)) {
-    int t, lim;
-    size_t qhead;
-    tile_of(u, t, qhead, lim);
-    copy_rows_swz<D>((const T*)p.q + qhead * D, t, lim, qb[buf], wave, lane);
-    copy_rows_swz<D>((const T*)p.dout + qhead * D, t, lim, ob[buf], wave, lane);
+  const int ph = max(per_head, 1);
+  auto advance = [&](Cur c) __attribute__((always_inline)) -> Cur {
+    ++c.u;
+    if (++c.t == t_begin + ph) c.t = t_begin, ++c.hq;
+    return c;
+  };
+  auto qhead_of = [&](const Cur& c) __attribute__((always_inline)) -> size_t {
+    return ((size_t)b * p.H + g * p.group + min(c.hq, p.group - 1)) * N;
+  };
+  auto copies = [&](const Cur& c, int buf) __attribute__((always_inline)) {
+    const size_t qhead = qhead_of(c);
+    const int lim = c.u < n_iter ? N : 0;
+    copy_rows_swz<D>((const T*)p.q + qhead * D, c.t, lim, qb[buf], wave, lane);
+    copy_rows_swz<D>((const T*)p.dout + qhead * D, c.t, lim, ob[buf], wave, lane);
   };
   float lreg = INFINITY, dlreg = 0.0f;
-  auto row_stats = [&](int u) __attribute__((always_inline)) {
+  auto row_stats = [&](const Cur& c) __attribute__((always_inline)) {
     if (tid < 32) {
-      int t, lim;
-      size_t qhead;
-      tile_of(u, t, qhead, lim);
-      const int row = 32 * t + tid;
-      const bool ok = row < lim;
+      const size_t qhead = qhead_of(c);
+      const int row = 32 * c.t + tid;
+      const bool ok = c.u < n_iter && row < N;
       lreg = ok ? p.lse2[qhead + row] : INFINITY;
       dlreg = ok ? p.delta[qhead + row] : 0.0f;
     }
   };
+  Cur c0{0, t_begin, 0};  // iteration u
+  Cur c1 = advance(c0);   // u + 1
+  Cur c2 = advance(c1);   // u + 2
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dk[db] = f32x16{}, dv[db] = f32x16{};
   if (n_iter > 0) {
-    row_stats(0);
-    copies(0, 0);
-    copies(1, 1);
+    row_stats(c0);
+    copies(c0, 0);
+    copies(c1, 1);
     wait_vmem_keep<2 * NCPW>();
     if (tid < 32) ls[0][tid] = lreg, dls[0][tid] = dlreg;
   }
@@ -2549,13 +2570,11 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   // key above some query row) and a ragged last key block (keys at or past
   // kl) need one; there the masked scores are set to -inf in place before
   // the exponentials, elsewhere the scores go straight through.
-  auto iter = [&](int u, auto bufc) __attribute__((always_inline)) {
+  auto iter = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value, nbuf = (buf + 1) % kBwdBufs;
-    int t, lim;
-    size_t qhead;
-    tile_of(u, t, qhead, lim);
-    row_stats(u + 1);
-    copies(u + 2, (buf + 2) % kBwdBufs);
+    const int t = c0.t;
+    row_stats(c1);
+    copies(c2, (buf + 2) % kBwdBufs);
     if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
       f32x16 s = {}, dp = {};
       two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
@@ -2586,10 +2605,13 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     wait_vmem_keep<2 * NCPW>();  // row stats u+1 and tile u+1 landed; tile u+2 may be in flight
     if (tid < 32) ls[nbuf][tid] = lreg, dls[nbuf][tid] = dlreg;
     __syncthreads();
+    c0 = c1;
+    c1 = c2;
+    c2 = advance(c2);
   };
   for (int u0 = 0; u0 < n_iter; u0 += kBwdBufs) {
     static_for<kBwdBufs>([&](auto qc) __attribute__((always_inline)) {
-      if (u0 + decltype(qc)::value < n_iter) iter(u0 + decltype(qc)::value, qc);  // workgroup-uniform
+      if (u0 + decltype(qc)::value < n_iter) iter(qc);  // workgroup-uniform
     });
   }
   wait_vmem();
