@@ -744,6 +744,11 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rs, unsigned c
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)dst, 16, byte_off, 0, 0, 0);
 }
 
+// The same for one dword per lane (lane i lands at dst + 4 i).
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t rs, unsigned char* dst, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)dst, 4, byte_off, 0, 0, 0);
+}
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // s_waitcnt vmcnt(N): all but the N most recent vector-memory loads are done
@@ -2478,8 +2483,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   constexpr int NCPW = TB / 1024 / kBwdWaves;
   __shared__ __attribute__((aligned(1024))) unsigned char qb[kBwdBufs][TB];
   __shared__ __attribute__((aligned(1024))) unsigned char ob[kBwdBufs][TB];
-  __shared__ __attribute__((aligned(16))) float ls[kBwdBufs][32];
-  __shared__ __attribute__((aligned(16))) float dls[kBwdBufs][32];
+  __shared__ __attribute__((aligned(16))) float ls[kBwdBufs][64];   // rows 0-31 used
+  __shared__ __attribute__((aligned(16))) float dls[kBwdBufs][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2540,14 +2545,18 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     copy_rows_swz<D>((const T*)p.q + qhead * D, c.t, lim, qb[buf], wave, lane);
     copy_rows_swz<D>((const T*)p.dout + qhead * D, c.t, lim, ob[buf], wave, lane);
   };
-  float lreg = INFINITY, dlreg = 0.0f;
-  auto row_stats = [&](const Cur& c) __attribute__((always_inline)) {
-    if (tid < 32) {
-      const size_t qhead = qhead_of(c);
-      const int row = 32 * c.t + tid;
-      const bool ok = c.u < n_iter && row < N;
-      lreg = ok ? p.lse2[qhead + row] : INFINITY;
-      dlreg = ok ? p.delta[qhead + row] : 0.0f;
+  // Row statistics of a query tile (lse2 = LSE * log2 e, and Delta) straight
+  // into LDS beside its Q and dO rows, issued by the last wave ahead of its
+  // tile copies: lanes 0-31 take the tile's rows; lanes 32-63, rows at or past
+  // N and every row past the last iteration fall outside the copy's range and
+  // land as zeros. Such rows have zero Q and dO rows too, so there P = 1 and
+  // dS = 0 exactly, and they add nothing to dK or dV.
+  auto stats_copy = [&](const Cur& c, int buf) __attribute__((always_inline)) {
+    if (wave == kBwdWaves - 1) {
+      const int rows = c.u < n_iter ? max(0, min(32, N - 32 * c.t)) : 0;
+      const size_t row0 = rows > 0 ? qhead_of(c) + 32 * c.t : 0;
+      lds_copy4(buffer_rsrc(p.lse2 + row0, rows * 4), (unsigned char*)ls[buf], 4 * lane);
+      lds_copy4(buffer_rsrc(p.delta + row0, rows * 4), (unsigned char*)dls[buf], 4 * lane);
     }
   };
   Cur c0{0, t_begin, 0};  // iteration u
@@ -2558,11 +2567,11 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
 #pragma unroll
   for (int db = 0; db < DB; ++db) dk[db] = f32x16{}, dv[db] = f32x16{};
   if (n_iter > 0) {
-    row_stats(c0);
+    stats_copy(c0, 0);
+    stats_copy(c1, 1);
     copies(c0, 0);
     copies(c1, 1);
-    wait_vmem_keep<2 * NCPW>();
-    if (tid < 32) ls[0][tid] = lreg, dls[0][tid] = dlreg;
+    wait_vmem_keep<2 * NCPW>();  // statistics of tiles 0 and 1 and tile 0 landed
   }
   __syncthreads();
   // Iteration u uses buffer u % 3, a compile-time index (the loop is unrolled
@@ -2571,9 +2580,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   // kl) need one; there the masked scores are set to -inf in place before
   // the exponentials, elsewhere the scores go straight through.
   auto iter = [&](auto bufc) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value, nbuf = (buf + 1) % kBwdBufs;
+    constexpr int buf = decltype(bufc)::value;
     const int t = c0.t;
-    row_stats(c1);
+    stats_copy(c2, (buf + 2) % kBwdBufs);
     copies(c2, (buf + 2) % kBwdBufs);
     if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
       f32x16 s = {}, dp = {};
@@ -2602,8 +2611,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
       tr_product<E, D>(ob[buf], sz, pf, dv);
       tr_product<E, D>(qb[buf], sz, dsf, dk);
     }
-    wait_vmem_keep<2 * NCPW>();  // row stats u+1 and tile u+1 landed; tile u+2 may be in flight
-    if (tid < 32) ls[nbuf][tid] = lreg, dls[nbuf][tid] = dlreg;
+    wait_vmem_keep<2 * NCPW>();  // tile u+1 and the statistics of u+2 landed; tile u+2 may be in flight
     __syncthreads();
     c0 = c1;
     c1 = c2;
