@@ -2206,6 +2206,9 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 #ifndef FA_BWD_KV_OCC
 #define FA_BWD_KV_OCC 2  // waves per SIMD the dK/dV pass is compiled for (1: 512 registers)
 #endif
+#ifndef FA_BWD_KV_SUB
+#define FA_BWD_KV_SUB 2  // dK/dV pass: 32-row query tiles per iteration (1: three buffers, 2: two)
+#endif
 #ifndef FA_BWD_LOOKAHEAD
 #define FA_BWD_LOOKAHEAD 2  // backward passes: LDS operand reads issued this many MFMAs ahead
 #endif
@@ -2479,12 +2482,16 @@ template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_dma(BwdParams p) {
   using T = typename E::T;
   using v8 = typename E::v8;
+  // An iteration takes SUB query tiles of 32 rows (one barrier, one set of
+  // copies and one cursor step for all of them); NB buffers of SUB tiles.
+  constexpr int SUB = FA_BWD_KV_SUB, NB = SUB == 1 ? 3 : 2, AHEAD = NB - 1;
   constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
-  constexpr int NCPW = TB / 1024 / kBwdWaves;
-  __shared__ __attribute__((aligned(1024))) unsigned char qb[kBwdBufs][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char ob[kBwdBufs][TB];
-  __shared__ __attribute__((aligned(16))) float ls[kBwdBufs][64];   // rows 0-31 used
-  __shared__ __attribute__((aligned(16))) float dls[kBwdBufs][64];
+  constexpr int NCPW = TB / 1024 / kBwdWaves;  // 1 KB copies per wave per 32-row tile and tensor
+  static_assert(SUB == 1 || SUB == 2, "one or two 32-row query tiles per iteration");
+  __shared__ __attribute__((aligned(1024))) unsigned char qb[NB][SUB * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char ob[NB][SUB * TB];
+  __shared__ __attribute__((aligned(16))) float ls[NB][64];  // rows 0 .. 32 SUB - 1 used
+  __shared__ __attribute__((aligned(16))) float dls[NB][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2502,8 +2509,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   kl = __builtin_amdgcn_readfirstlane(kl);
   const int k_wg0 = kt * kBwdRows, kw0 = k_wg0 + 32 * wave, key = kw0 + l32;
   const int nqt = (N + 31) / 32;
-  const int t_begin = CAUSAL ? k_wg0 / 32 : 0;
-  const int per_head = k_wg0 < kl ? nqt - t_begin : 0;
+  const int t_begin = CAUSAL ? k_wg0 / 32 : 0;  // a multiple of 4: iterations start at even tiles
+  const int per_head = k_wg0 < kl ? (nqt - t_begin + SUB - 1) / SUB : 0;  // iterations per head
   const int n_iter = per_head * p.group;
   const bool wave_live = kw0 < kl;
 
@@ -2522,18 +2529,19 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   SwzTile<D> sz;
   sz.init(pinned_int(lane));
 
-  // iteration u: query head g*group + u / per_head, query tile t_begin + u % per_head
-  // Cursor of iteration u: query tile t and query head hq (index within the
-  // group) of a scan that runs over t in [t_begin, t_begin + per_head) for each
-  // head of the group in turn; advanced by one per iteration (no division in
-  // the loop). Past n_iter the head index is clamped and the row limit is 0.
+  // Cursor of iteration u: first query tile t and query head hq (index within
+  // the group) of a scan that runs over t in [t_begin, t_begin + SUB per_head)
+  // in steps of SUB for each head of the group in turn; advanced once per
+  // iteration (no division in the loop). Past n_iter the head index is
+  // clamped and the row limit is 0.
   struct Cur {
     int u, t, hq;
   };
   const int ph = max(per_head, 1);
   auto advance = [&](Cur c) __attribute__((always_inline)) -> Cur {
     ++c.u;
-    if (++c.t == t_begin + ph) c.t = t_begin, ++c.hq;
+    c.t += SUB;
+    if (c.t == t_begin + SUB * ph) c.t = t_begin, ++c.hq;
     return c;
   };
   auto qhead_of = [&](const Cur& c) __attribute__((always_inline)) -> size_t {
@@ -2542,18 +2550,22 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   auto copies = [&](const Cur& c, int buf) __attribute__((always_inline)) {
     const size_t qhead = qhead_of(c);
     const int lim = c.u < n_iter ? N : 0;
-    copy_rows_swz<D>((const T*)p.q + qhead * D, c.t, lim, qb[buf], wave, lane);
-    copy_rows_swz<D>((const T*)p.dout + qhead * D, c.t, lim, ob[buf], wave, lane);
+#pragma unroll
+    for (int x = 0; x < SUB; ++x) {
+      copy_rows_swz<D>((const T*)p.q + qhead * D, c.t + x, lim, qb[buf] + x * TB, wave, lane);
+      copy_rows_swz<D>((const T*)p.dout + qhead * D, c.t + x, lim, ob[buf] + x * TB, wave, lane);
+    }
   };
-  // Row statistics of a query tile (lse2 = LSE * log2 e, and Delta) straight
-  // into LDS beside its Q and dO rows, issued by the last wave ahead of its
-  // tile copies: lanes 0-31 take the tile's rows; lanes 32-63, rows at or past
-  // N and every row past the last iteration fall outside the copy's range and
-  // land as zeros. Such rows have zero Q and dO rows too, so there P = 1 and
-  // dS = 0 exactly, and they add nothing to dK or dV.
+  // Row statistics of an iteration's rows (lse2 = LSE * log2 e, and Delta)
+  // straight into LDS beside its Q and dO rows, issued by the last wave ahead
+  // of its tile copies: lane i takes row 32 t + i; lanes past the
+  // iteration's rows, rows at or past N and every row past the last
+  // iteration fall outside the copy's range and land as zeros. Such rows have
+  // zero Q and dO rows too, so there P = 1 and dS = 0 exactly, and they add
+  // nothing to dK or dV.
   auto stats_copy = [&](const Cur& c, int buf) __attribute__((always_inline)) {
     if (wave == kBwdWaves - 1) {
-      const int rows = c.u < n_iter ? max(0, min(32, N - 32 * c.t)) : 0;
+      const int rows = c.u < n_iter ? max(0, min(32 * SUB, N - 32 * c.t)) : 0;
       const size_t row0 = rows > 0 ? qhead_of(c) + 32 * c.t : 0;
       lds_copy4(buffer_rsrc(p.lse2 + row0, rows * 4), (unsigned char*)ls[buf], 4 * lane);
       lds_copy4(buffer_rsrc(p.delta + row0, rows * 4), (unsigned char*)dls[buf], 4 * lane);
@@ -2568,57 +2580,66 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   for (int db = 0; db < DB; ++db) dk[db] = f32x16{}, dv[db] = f32x16{};
   if (n_iter > 0) {
     stats_copy(c0, 0);
-    stats_copy(c1, 1);
+    if constexpr (AHEAD == 2) stats_copy(c1, 1);
     copies(c0, 0);
-    copies(c1, 1);
-    wait_vmem_keep<2 * NCPW>();  // statistics of tiles 0 and 1 and tile 0 landed
+    if constexpr (AHEAD == 2) copies(c1, 1);
+    // statistics and the tiles of iteration 0 landed (those of 1 may be in flight)
+    wait_vmem_keep<(AHEAD - 1) * 2 * NCPW * SUB>();
   }
   __syncthreads();
-  // Iteration u uses buffer u % 3, a compile-time index (the loop is unrolled
-  // over the three buffers). Masks: only the wave's diagonal query tile (some
-  // key above some query row) and a ragged last key block (keys at or past
-  // kl) need one; there the masked scores are set to -inf in place before
+  // Iteration u uses buffer u % NB, a compile-time index (the loop is
+  // unrolled over the buffers). Masks: only the wave's diagonal query tile
+  // (some key above some query row) and a ragged last key block (keys at or
+  // past kl) need one; there the masked scores are set to -inf in place before
   // the exponentials, elsewhere the scores go straight through.
   auto iter = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int t = c0.t;
-    stats_copy(c2, (buf + 2) % kBwdBufs);
-    copies(c2, (buf + 2) % kBwdBufs);
-    if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
-      f32x16 s = {}, dp = {};
-      two_products<E, D>(qb[buf], ob[buf], sz, hi, kf, vf, s, dp);
-      if ((CAUSAL && 32 * t < kw0 + 31) || kw0 + 32 > kl) {
+    const Cur& ca = AHEAD == 2 ? c2 : c1;
+    stats_copy(ca, (buf + AHEAD) % NB);
+    copies(ca, (buf + AHEAD) % NB);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qry = 32 * t + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const bool ok = key < kl && (!CAUSAL || key <= qry);
-          s[i] = ok ? s[i] : -INFINITY;
+    for (int x = 0; x < SUB; ++x) {
+      const int t = c0.t + x;
+      const unsigned char* qt = qb[buf] + x * TB;
+      const unsigned char* ot = ob[buf] + x * TB;
+      if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
+        f32x16 s = {}, dp = {};
+        two_products<E, D>(qt, ot, sz, hi, kf, vf, s, dp);
+        if ((CAUSAL && 32 * t < kw0 + 31) || kw0 + 32 > kl) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qry = 32 * t + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const bool ok = key < kl && (!CAUSAL || key <= qry);
+            s[i] = ok ? s[i] : -INFINITY;
+          }
         }
-      }
-      v8 pf[2], dsf[2];
+        v8 pf[2], dsf[2];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = *(const f32x4*)(&ls[buf][8 * q4 + 4 * hi]);
-        const f32x4 d4 = *(const f32x4*)(&dls[buf][8 * q4 + 4 * hi]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 l4 = *(const f32x4*)(&ls[buf][32 * x + 8 * q4 + 4 * hi]);
+          const f32x4 d4 = *(const f32x4*)(&dls[buf][32 * x + 8 * q4 + 4 * hi]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * q4 + e;
-          const float pr = fast_exp2(fmaf(s[i], c, -l4[e]));
-          pf[i >> 3][i & 7] = E::cvt(pr);
-          dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            const float pr = fast_exp2(fmaf(s[i], c, -l4[e]));
+            pf[i >> 3][i & 7] = E::cvt(pr);
+            dsf[i >> 3][i & 7] = E::cvt(pr * (dp[i] - d4[e]));
+          }
         }
+        tr_product<E, D>(ot, sz, pf, dv);
+        tr_product<E, D>(qt, sz, dsf, dk);
       }
-      tr_product<E, D>(ob[buf], sz, pf, dv);
-      tr_product<E, D>(qb[buf], sz, dsf, dk);
     }
-    wait_vmem_keep<2 * NCPW>();  // tile u+1 and the statistics of u+2 landed; tile u+2 may be in flight
+    // the next iteration's tiles and statistics landed (the copies issued
+    // here may stay in flight when they run two iterations ahead)
+    wait_vmem_keep<(AHEAD - 1) * 2 * NCPW * SUB>();
     __syncthreads();
     c0 = c1;
     c1 = c2;
     c2 = advance(c2);
   };
-  for (int u0 = 0; u0 < n_iter; u0 += kBwdBufs) {
-    static_for<kBwdBufs>([&](auto qc) __attribute__((always_inline)) {
+  for (int u0 = 0; u0 < n_iter; u0 += NB) {
+    static_for<NB>([&](auto qc) __attribute__((always_inline)) {
       if (u0 + decltype(qc)::value < n_iter) iter(qc);  // workgroup-uniform
     });
   }
