@@ -725,14 +725,12 @@ __device__ __forceinline__ int v_swz(int r) {
   return (r & 3) << 1;
 }
 
-// Four e4m3 codes -> four bf16 (exact): hardware fp8->f32 convert, keep the
-// high halves (an e4m3 value has at most 4 significant bits).
+// Four e4m3 codes -> four bf16, exact: every e4m3 value (4 significant bits,
+// exponents 2^-9 .. 2^8) is a bf16 value; two codes per convert, scale 1.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(unsigned w) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
   u32x2 r;
-  r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-  r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+  r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   return r;
 }
 

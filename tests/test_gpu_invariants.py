@@ -126,3 +126,33 @@ def test_grouped_heads_equal_repeated_heads_bit_for_bit(dtype, N, causal):
     o_r, lse_r = fa.forward(q, k_r, v_r, 0.125, causal, None, descale=w.descale)
     torch.cuda.synchronize()
     assert torch.equal(o_g, o_r) and torch.equal(lse_g, lse_r)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_fp8", "fa_fwd_fp8_p8"])
+@pytest.mark.parametrize("N,causal", [(300, True), (4096, False)])
+def test_fp8_every_v_code_reaches_o_exactly(entry, N, causal):
+    """key_len 1: every query row's only weight is 1 (on key 0), so O is V's row
+    0 decoded with V's descale of 1, exactly. Row 0 of V holds every finite e4m3
+    code (the two NaN codes replaced by 0) over the two batch entries, so each
+    code's conversion to the P V operand is checked. N 300 causal runs the
+    fp8 direct-to-LDS kernel, N 4096 the pipelined one (fa_fwd_fp8)."""
+    B, H, d = 2, 1, 128
+    g = torch.Generator().manual_seed(7)
+    codes = torch.arange(256, dtype=torch.int32).reshape(B, d)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    v8 = (torch.randint(0, 256, (B, H, N, d), generator=g, dtype=torch.int32) & 0x77)
+    v8[:, 0, 0, :] = codes
+    q = (torch.randn(B, H, N, d, generator=g) * 4).to(torch.float8_e4m3fn)
+    k = (torch.randn(B, H, N, d, generator=g) * 4).to(torch.float8_e4m3fn)
+    v = v8.to(torch.uint8).view(torch.float8_e4m3fn)
+    expect = v[:, 0, 0, :].float()
+    q, k, v = (t.to(DEV) for t in (q, k, v))
+    o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=DEV)
+    kl = torch.ones(B, dtype=torch.int32, device=DEV)
+    say(f"case fp8 every code entry={entry} N={N} causal={causal}")
+    getattr(fa, entry)(q, k, v, o, lse, 1.0 / math.sqrt(d), causal, kl)
+    torch.cuda.synchronize()
+    got = o.float().cpu()
+    for b in range(B):
+        assert torch.equal(got[b, 0], expect[b].expand(N, d)), f"batch {b}"
