@@ -2528,18 +2528,24 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   sz.init(pinned_int(lane));
 
   // Cursor of iteration u: first query tile t and query head hq (index within
-  // the group) of a scan that runs over t in [t_begin, t_begin + SUB per_head)
-  // in steps of SUB for each head of the group in turn; advanced once per
-  // iteration (no division in the loop). Past n_iter the head index is
-  // clamped and the row limit is 0.
+  // the group) of a scan that runs over t from t_begin + SUB (per_head - 1)
+  // down to t_begin in steps of SUB, for each head of the group in turn;
+  // advanced once per iteration (no division in the loop). Past n_iter the
+  // head index is clamped and the row limit is 0. Descending order: every
+  // workgroup of a head starts at the head's last query tiles whatever its
+  // key block, so the workgroups running together on an XCD read the same
+  // Q / dO tile at about the same time and fetch it through L2 once (in
+  // ascending order each would start at its own diagonal and read a
+  // different tile).
   struct Cur {
     int u, t, hq;
   };
   const int ph = max(per_head, 1);
+  const int t_last = t_begin + SUB * (ph - 1);
   auto advance = [&](Cur c) __attribute__((always_inline)) -> Cur {
     ++c.u;
-    c.t += SUB;
-    if (c.t == t_begin + SUB * ph) c.t = t_begin, ++c.hq;
+    c.t -= SUB;
+    if (c.t < t_begin) c.t = t_last, ++c.hq;
     return c;
   };
   auto qhead_of = [&](const Cur& c) __attribute__((always_inline)) -> size_t {
@@ -2569,9 +2575,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
       lds_copy4(buffer_rsrc(p.delta + row0, rows * 4), (unsigned char*)dls[buf], 4 * lane);
     }
   };
-  Cur c0{0, t_begin, 0};  // iteration u
-  Cur c1 = advance(c0);   // u + 1
-  Cur c2 = advance(c1);   // u + 2
+  Cur c0{0, t_last, 0};  // iteration u
+  Cur c1 = advance(c0);  // u + 1
+  Cur c2 = advance(c1);  // u + 2
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
