@@ -2191,10 +2191,11 @@ __global__ __launch_bounds__(64) void attn_decode_merge(DecodeParams p) {
 //
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),  Delta = rowsum(dO * O),
 //   dQ = scale * dS K,  dK = scale * dS^T Q,  P = exp2(c*s - LSE*log2(e)).
-// Three passes on one stream: attn_bwd_prep writes Delta and LSE*log2(e) per
-// query row; attn_bwd_dq_dma gives every wave 32 query rows and streams the
-// 32-key K/V tiles (the forward's orientation: lanes own queries, so LSE and
-// Delta are per-lane values); attn_bwd_dkdv_dma gives every wave 32 keys and
+// Two passes on one stream: attn_bwd_dq_dma gives every wave 32 query rows
+// and streams the 32-key K/V tiles (the forward's orientation: lanes own
+// queries, so LSE and Delta are per-lane values; it computes Delta and
+// LSE*log2(e) of its rows and stores them for the next pass);
+// attn_bwd_dkdv_dma gives every wave 32 keys and
 // streams 32-query Q/dO tiles over the query heads that share its K/V head
 // (lanes own keys, so dK and dV accumulate with no cross-wave reduction and
 // no atomics). Both recompute S; products whose second operand comes out of
@@ -2225,30 +2226,6 @@ __device__ __forceinline__ int bwd_block() {
 constexpr int kBwdWaves = FA_BWD_WAVES;    // waves per workgroup
 constexpr int kBwdRows = kBwdWaves * 32;   // query rows (dQ) or keys (dK/dV) per workgroup
 
-// Delta and LSE * log2(e) of every query row: D/8 lanes per row, 16 bytes each.
-template <class T, int D>
-__global__ __launch_bounds__(256) void attn_bwd_prep(BwdParams p) {
-  typedef T v8t __attribute__((ext_vector_type(8)));
-  constexpr int LPR = D / 8, RPB = 256 / LPR;
-  const long long rows = (long long)p.B * p.H * p.N;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  float acc = 0.0f;
-  if (row < rows) {
-    const v8t a = *(const v8t*)((const T*)p.dout + row * D + 8 * part);
-    const v8t b = *(const v8t*)((const T*)p.o + row * D + 8 * part);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-  }
-#pragma unroll
-  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 64);
-  if (row < rows && part == 0) {
-    p.delta[row] = acc;
-    const float L = p.lse[row];
-    p.lse2[row] = L == -INFINITY ? INFINITY : L * 1.4426950408889634f;
-  }
-}
-
 // The row's 16 accumulator values scaled and written as 4-element runs: lane
 // owns column `col` of the D-layout tile, rows are the head-dim elements.
 template <class T, int DB>
@@ -2267,13 +2244,14 @@ __device__ __forceinline__ void store_grad(T* row_ptr, int hi, float scale, cons
 
 // ---------------------------------------------------------------------------
 // The streamed 32-row tiles of both passes reach LDS through buffer_load ...
-// lds (no staging registers), three buffers deep, so a tile's copy is issued
-// two iterations before it is used. Every tile is stored with
-// the V-operand slot permutation (v_swz): transposing reads use it as the
-// forward's V reads do, and row reads (the A operands of S and dP) look their
-// 16-byte slot up through the same permutation.
+// lds (no staging registers): four buffers in the dQ pass (a tile's copy is
+// issued three iterations before its dQ product and two before its S and dP
+// products), two buffers of two tiles in the dK/dV pass (one iteration
+// ahead). Every tile is stored with the V-operand slot permutation (v_swz):
+// transposing reads use it as the forward's V reads do, and row reads (the A
+// operands of S and dP) look their 16-byte slot up through the same
+// permutation.
 // ---------------------------------------------------------------------------
-constexpr int kBwdBufs = 3;
 
 template <int D>
 struct SwzTile {
@@ -2411,8 +2389,31 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
     }
   }
   const bool row_ok = qrow < N;
-  const float lse2 = row_ok ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
-  const float dl = row_ok ? p.delta[(size_t)bh * N + qrow] : 0.0f;
+  // Delta = rowsum(dO * O) and LSE * log2 e of this lane's query row: the
+  // lane and its partner l ^ 32 hold the two halves of the row's dO, so each
+  // reads the same half of O, and the two partial sums meet in one lane
+  // exchange. Both are stored for the dK/dV pass (which runs after this one);
+  // rows at or past N read as zeros and are not stored.
+  float dl = 0.0f, lse2 = INFINITY;
+  {
+    const auto ro = tile_rsrc((const T*)p.o + head, 0, N, N, D * 2);
+    float acc = 0.0f;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const v8 of = __builtin_bit_cast(v8, load16(ro, qrow * D * 2 + 32 * st + 16 * hi));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)df[st][e], (float)of[e], acc);
+    }
+    dl = sum_halves(acc);
+    if (row_ok) {
+      const float L = p.lse[(size_t)bh * N + qrow];
+      lse2 = L == -INFINITY ? INFINITY : L * 1.4426950408889634f;
+      if (hi == 0) {
+        p.delta[(size_t)bh * N + qrow] = dl;
+        p.lse2[(size_t)bh * N + qrow] = lse2;
+      }
+    }
+  }
   const float c = p.c;
   SwzTile<D> sz;
   sz.init(pinned_int(lane));
@@ -2824,17 +2825,13 @@ template <class E, int D, bool C>
 hipError_t launch_backward_t(const BwdParams& p, hipStream_t stream) {
   BwdParams local = p;
   void* args[] = {&local};
-  const long long rows = (long long)p.B * p.H * p.N;
-  const long long g_prep = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
   const long long g_dq = (long long)p.B * p.H * p.n_qt;
   const long long g_kv = (long long)p.B * p.H_kv * p.n_kt;
-  if (g_prep > 0x7fffffffLL || g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL)
-    return hipErrorInvalidConfiguration;
-  hipError_t e = hipLaunchKernel((const void*)attn_bwd_prep<typename E::T, D>, dim3((unsigned)g_prep),
-                                 dim3(256), args, 0, stream);
-  if (e != hipSuccess) return e;
-  e = hipLaunchKernel((const void*)attn_bwd_dq_dma<E, D, C>, dim3((unsigned)g_dq),
-                      dim3(kBwdWaves * 64), args, 0, stream);
+  if (g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // the dQ pass also writes every row's Delta and LSE * log2 e to the
+  // workspace, which the dK/dV pass (queued after it) reads
+  hipError_t e = hipLaunchKernel((const void*)attn_bwd_dq_dma<E, D, C>, dim3((unsigned)g_dq),
+                                 dim3(kBwdWaves * 64), args, 0, stream);
   if (e != hipSuccess) return e;
   return hipLaunchKernel((const void*)attn_bwd_dkdv_dma<E, D, C>, dim3((unsigned)g_kv),
                          dim3(kBwdWaves * 64), args, 0, stream);

@@ -302,7 +302,8 @@ int fa_fwd_decode_noalloc(const void* Q, const void* K, const void* V, void* O, 
  *   d        64 or 128
  *   other arguments as fa_fwd_gqa (H_kv == H for ungrouped heads).
  * Errors as fa_fwd, plus FA_ERR_INVALID_ARG for a NULL, misaligned or too
- * small workspace. Three kernels run in order on `stream`.
+ * small workspace. Two kernels run in order on `stream` (the first also
+ * writes the rows' Delta and LSE * log2 e to the workspace for the second).
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int H_kv, int N, int d,
