@@ -265,7 +265,7 @@ def main(argv=None):
         print(json.dumps({"error": "--p8 applies to fp8 workloads"}))
         return 2
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; "
+        print(json.dumps({"error": "the benchmark measures one GPU; "
                                    "multi-GPU runs are not supported (use --gpus 1)"}))
         return 2
 
