@@ -395,6 +395,55 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[SB], float c, float t
   l += rs;
 }
 
+// The same update with a lazy reference maximum (no row maximum per tile):
+// P = exp2(c*s + base), base = -m*c, is formed against the row's current
+// reference m, and the row sum of P that l needs anyway tells whether a score
+// got too far above m. If a lane's partial sum exceeds E::kPBound, or is
+// inf / NaN (the first live tile, while m = -inf and base = +inf), a rarely
+// taken branch takes the tile's true row maximum, moves m there, rescales O
+// and l and recomputes P. Otherwise every P is at most E::kPBound, which the
+// 16-bit P and the fp32 accumulators hold without loss; O / l is the same
+// exact softmax for any reference.
+template <class E, int SB, int DB>
+__device__ __forceinline__ void lazy_softmax(f32x16 (&s)[SB], float c, float& m, float& base,
+                                             float& l, f32x16 (&o)[DB],
+                                             typename E::v8 (&pf)[SB * 2]) {
+  float rs = 0.0f;
+#pragma unroll
+  for (int ps = 0; ps < SB * 2; ++ps) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pf[ps][e] = E::cvt(fast_exp2(fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, base)));
+    rs = E::sum8(pf[ps], rs);
+  }
+  if (__builtin_amdgcn_ballot_w64(!(rs <= E::kPBound)) != 0) {
+    float x = s[0][0];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x = fmaxf(x, s[sb][i]);
+    const float mn = fmaxf(m, max_halves(x));
+    const float alpha = pinned(mn == m ? 1.0f : fast_exp2((m - mn) * c));  // exp2(-inf) = 0
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    m = mn;
+    base = -mn * c;
+    const float bu = mn == -INFINITY ? 0.0f : base;  // a row with no live key yet: P = 0
+    rs = 0.0f;
+#pragma unroll
+    for (int ps = 0; ps < SB * 2; ++ps) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pf[ps][e] = E::cvt(fast_exp2(fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, bu)));
+      rs = E::sum8(pf[ps], rs);
+    }
+  }
+  l += rs;
+}
+
 // Key index of accumulator element i of 32-key block sb for this lane half.
 __device__ __forceinline__ int acc_row(int sb, int i, int hi) {
   return 32 * sb + 8 * (i >> 2) + 4 * hi + (i & 3);
@@ -887,8 +936,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.0f;
-  const float thr = fminf(kRescaleLog2 / p.c, 1e30f);
+  // m: reference maximum (raw score units); base = -m * c, +inf while m = -inf
+  float m = -INFINITY, base = INFINITY, l = 0.0f;
 
   auto tile = [&](int j, const unsigned char* kb, const unsigned char* vb, auto masked)
       __attribute__((always_inline)) {
@@ -921,7 +970,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_16bit_dma(Params p) {
         apply_mask<SB, CAUSAL>(s, j * BC, rr.kl, rr.qrow, hi);
     }
     v8 pf[PS];
-    online_softmax<E, SB, DB>(s, p.c, thr, m, l, o, pf);
+    lazy_softmax<E, SB, DB>(s, p.c, m, base, l, o, pf);
     // O += P V, operand reads LA steps ahead
 #pragma unroll
     for (int t = LA; t < NPV + LA; ++t) {
@@ -1283,6 +1332,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe(Params p) {
     l += rs;
   };
 
+  // P of the item's first half, while m is still -inf: the reference is set
+  // from this half's true row maximum at once (O and l are still zero), with
+  // no first try against m.
+  auto first_probs = [&](f32x16& s, v8 (&pf)[2], auto masked) __attribute__((always_inline)) {
+    if constexpr (decltype(masked)::value) mask_half(s, 0);
+    float x = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) x = fmaxf(x, s[i]);
+    m = max_halves(x);
+    base = -m * c;
+    const float bu = m == -INFINITY ? 0.0f : base;
+    float rs = 0.0f;
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[ps][e] = E::cvt(fast_exp2(fmaf(s[8 * ps + e], c, bu)));
+      rs = E::sum8(pf[ps], rs);
+    }
+    l = rs;
+  };
+
   f32x16 sa, sb;
   v8 pfa[2], pfb[2];
   // The S product of half h of the K tile at kb (when hn) and O += V^T P^T of
@@ -1374,8 +1444,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe(Params p) {
   if (rr.wnt > 0) {
     scores(k0s, 0, sa);
     scores(k0s, 1, sb);
-    if (0 < rr.wfull) probs(sa, pfa, 0, std::false_type{});
-    else probs(sa, pfa, 0, std::true_type{});
+    if (0 < rr.wfull) first_probs(sa, pfa, std::false_type{});
+    else first_probs(sa, pfa, std::true_type{});
   }
   __syncthreads();  // K of tile 0 is read by every wave before its buffer is refilled
   // Iterations [0, ts): every half unmasked and a next tile to score; two of
