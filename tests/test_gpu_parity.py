@@ -114,14 +114,16 @@ def test_fp32_outlier_keys():
         assert same_inf and mx <= 4e-5 and mean <= 1e-6 and dl <= 1e-5
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp8", "fp32"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("fp16", 64), ("fp16", 128),
+                                     ("fp8", 128), ("fp32", 64)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_running_max_keeps_growing(dtype, causal):
+def test_running_max_keeps_growing(dtype, d, causal):
     """Keys scaled up along the sequence so every key tile raises the row
     maxima, by small and by very large steps: the running-max correction
-    (and its threshold) must reproduce the exact softmax."""
-    d = 128 if dtype == "fp8" else 64
-    spec = small_spec(dtype, d, 700, causal, True, B=2, H=2, seed=8300 + causal, outliers=False)
+    (and its threshold, or the lazy reference's sum check) must reproduce the
+    exact softmax. Causal 16-bit inputs at this length take the direct-to-LDS
+    kernel, the others the pipelined or register-staged ones."""
+    spec = small_spec(dtype, d, 700, causal, True, B=2, H=2, seed=8300 + causal + d, outliers=False)
     w = W.draw(spec)
     grow = torch.linspace(0.2, 6.0, spec.N).reshape(1, 1, spec.N, 1)
     if dtype == "fp8":
