@@ -2575,6 +2575,12 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   __shared__ __attribute__((aligned(1024))) unsigned char ob[NB][SUB * TB];
   __shared__ __attribute__((aligned(16))) float ls[NB][64];  // rows 0 .. 32 SUB - 1 used
   __shared__ __attribute__((aligned(16))) float dls[NB][64];
+  // NKL of the wave's K operands live in LDS instead of registers (d = 128:
+  // with all of them in registers the pass needs a few more than the 256 it
+  // has, and the compiler's scratch reloads of the spilled ones in the loop
+  // wait on the vector-memory counter, that is on the tile copies in flight).
+  constexpr int NKL = D == 128 ? 2 : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char kres[kBwdWaves][NKL > 0 ? NKL * 1024 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2608,6 +2614,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
       vf[st] = __builtin_bit_cast(v8, load16(rv, key * D * 2 + 32 * st + 16 * hi));
     }
   }
+#pragma unroll
+  for (int st = 0; st < NKL; ++st) *(v8*)(kres[wave] + st * 1024 + lane * 16) = kf[st];
   const float c = p.c;
   SwzTile<D> sz;
   sz.init(pinned_int(lane));
@@ -2693,7 +2701,17 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
       const unsigned char* ot = ob[buf] + x * TB;
       if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
         f32x16 s = {}, dp = {};
-        two_products<E, D>(qt, ot, sz, hi, kf, vf, s, dp);
+        v8 kk[KS];
+        {
+          // an offset the compiler cannot see through: the operands are read
+          // back from LDS here, not kept live in registers from the store
+          int ko = lane * 16;
+          __asm__ volatile("" : "+v"(ko));
+#pragma unroll
+          for (int st = 0; st < KS; ++st)
+            kk[st] = st < NKL ? *(const v8*)(kres[wave] + st * 1024 + ko) : kf[st];
+        }
+        two_products<E, D>(qt, ot, sz, hi, kk, vf, s, dp);
         if ((CAUSAL && 32 * t < kw0 + 31) || kw0 + 32 > kl) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
