@@ -2431,8 +2431,18 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
   constexpr int NCPW = TB / 1024 / kBwdWaves;  // copies per wave per tile and tensor
   constexpr int NB = 4;  // K / V buffers: tile j + 3 is copied while j and j + 1 are read
-  __shared__ __attribute__((aligned(1024))) unsigned char kb[NB][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char vb[NB][TB];
+  // One named array per buffer: distinct objects let the compiler see that
+  // the copies in flight into one buffer cannot alias the operand reads from
+  // another, so those reads do not wait for the copies to land.
+  __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB], k1s[TB], k2s[TB], k3s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0s[TB], v1s[TB], v2s[TB], v3s[TB];
+  static_assert(NB == 4, "four named buffers per operand");
+  auto kb = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? k0s : i == 1 ? k1s : i == 2 ? k2s : k3s;
+  };
+  auto vb = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? v0s : i == 1 ? v1s : i == 2 ? v2s : v3s;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2503,8 +2513,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   sz.init(pinned_int(lane));
 
   auto copies = [&](int j, int buf) __attribute__((always_inline)) {
-    copy_rows_swz<D>(Kh, j, kv_end, kb[buf], wave, lane);
-    copy_rows_swz<D>(Vh, j, kv_end, vb[buf], wave, lane);
+    copy_rows_swz<D>(Kh, j, kv_end, kb(buf), wave, lane);
+    copy_rows_swz<D>(Vh, j, kv_end, vb(buf), wave, lane);
   };
   f32x16 dq[DB];
 #pragma unroll
@@ -2525,7 +2535,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
   // addresses are compile-time, and the S / dP registers of consecutive tiles
   // alternate between two sets (sp[j % 2], dpp[j % 2]) with no copies.
   f32x16 sp[2][1] = {{f32x16{}}, {f32x16{}}}, dpp[2] = {f32x16{}, f32x16{}};
-  two_products<E, D>(kb[0], vb[0], sz, hi, qf, df, sp[0][0], dpp[0]);
+  two_products<E, D>(kb(0), vb(0), sz, hi, qf, df, sp[0][0], dpp[0]);
   auto tile = [&](int j, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value, nb1 = (buf + 1) % NB, x = buf & 1;
     f32x16 (&s)[1] = sp[x];
@@ -2533,7 +2543,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
     if (j >= wfull) apply_mask<1, CAUSAL>(s, 32 * j, kl, qrow, hi);
     sp[x ^ 1][0] = f32x16{};
     dpp[x ^ 1] = f32x16{};
-    two_products<E, D>(kb[nb1], vb[nb1], sz, hi, qf, df, sp[x ^ 1][0], dpp[x ^ 1]);
+    two_products<E, D>(kb(nb1), vb(nb1), sz, hi, qf, df, sp[x ^ 1][0], dpp[x ^ 1]);
     v8 ds[2];
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps)
@@ -2543,7 +2553,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void attn_bwd_dq_dma(BwdParams p
         const float pr = fast_exp2(fmaf(s[0][i], c, -lse2));
         ds[ps][e] = E::cvt(pr * (dp[i] - dl));
       }
-    tr_product<E, D>(kb[buf], sz, ds, dq);
+    tr_product<E, D>(kb(buf), sz, ds, dq);
   };
   for (int j0 = 0; j0 < nt; j0 += NB) {
     static_for<NB>([&](auto qc) __attribute__((always_inline)) {
@@ -2571,10 +2581,23 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
   constexpr int KS = D / 16, DB = D / 32, TB = 32 * D * 2;
   constexpr int NCPW = TB / 1024 / kBwdWaves;  // 1 KB copies per wave per 32-row tile and tensor
   static_assert(SUB == 1 || SUB == 2, "one or two 32-row query tiles per iteration");
-  __shared__ __attribute__((aligned(1024))) unsigned char qb[NB][SUB * TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char ob[NB][SUB * TB];
-  __shared__ __attribute__((aligned(16))) float ls[NB][64];  // rows 0 .. 32 SUB - 1 used
-  __shared__ __attribute__((aligned(16))) float dls[NB][64];
+  // One named array per buffer (the third only when NB = 3): distinct
+  // objects let the compiler see that the copies in flight into one buffer
+  // cannot alias the reads from another, so those reads do not wait for them.
+  constexpr int QB3 = NB > 2 ? SUB * TB : 16, LS3 = NB > 2 ? 64 : 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char q0s[SUB * TB], q1s[SUB * TB], q2s[QB3];
+  __shared__ __attribute__((aligned(1024))) unsigned char o0s[SUB * TB], o1s[SUB * TB], o2s[QB3];
+  // row statistics, rows 0 .. 32 SUB - 1 used
+  __shared__ __attribute__((aligned(16))) float l0s[64], l1s[64], l2s[LS3];
+  __shared__ __attribute__((aligned(16))) float d0s[64], d1s[64], d2s[LS3];
+  auto qb = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? q0s : i == 1 ? q1s : q2s;
+  };
+  auto ob = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? o0s : i == 1 ? o1s : o2s;
+  };
+  auto ls = [&](int i) __attribute__((always_inline)) -> float* { return i == 0 ? l0s : i == 1 ? l1s : l2s; };
+  auto dls = [&](int i) __attribute__((always_inline)) -> float* { return i == 0 ? d0s : i == 1 ? d1s : d2s; };
   // NKL of the wave's K operands live in LDS instead of registers (d = 128:
   // with all of them in registers the pass needs a few more than the 256 it
   // has, and the compiler's scratch reloads of the spilled ones in the loop
@@ -2649,8 +2672,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     const int lim = c.u < n_iter ? N : 0;
 #pragma unroll
     for (int x = 0; x < SUB; ++x) {
-      copy_rows_swz<D>((const T*)p.q + qhead * D, c.t + x, lim, qb[buf] + x * TB, wave, lane);
-      copy_rows_swz<D>((const T*)p.dout + qhead * D, c.t + x, lim, ob[buf] + x * TB, wave, lane);
+      copy_rows_swz<D>((const T*)p.q + qhead * D, c.t + x, lim, qb(buf) + x * TB, wave, lane);
+      copy_rows_swz<D>((const T*)p.dout + qhead * D, c.t + x, lim, ob(buf) + x * TB, wave, lane);
     }
   };
   // Row statistics of an iteration's rows (lse2 = LSE * log2 e, and Delta)
@@ -2664,8 +2687,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
     if (wave == kBwdWaves - 1) {
       const int rows = c.u < n_iter ? max(0, min(32 * SUB, N - 32 * c.t)) : 0;
       const size_t row0 = rows > 0 ? qhead_of(c) + 32 * c.t : 0;
-      lds_copy4(buffer_rsrc(p.lse2 + row0, rows * 4), (unsigned char*)ls[buf], 4 * lane);
-      lds_copy4(buffer_rsrc(p.delta + row0, rows * 4), (unsigned char*)dls[buf], 4 * lane);
+      lds_copy4(buffer_rsrc(p.lse2 + row0, rows * 4), (unsigned char*)ls(buf), 4 * lane);
+      lds_copy4(buffer_rsrc(p.delta + row0, rows * 4), (unsigned char*)dls(buf), 4 * lane);
     }
   };
   Cur c0{0, t_last, 0};  // iteration u
@@ -2697,8 +2720,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
 #pragma unroll
     for (int x = 0; x < SUB; ++x) {
       const int t = c0.t + x;
-      const unsigned char* qt = qb[buf] + x * TB;
-      const unsigned char* ot = ob[buf] + x * TB;
+      const unsigned char* qt = qb(buf) + x * TB;
+      const unsigned char* ot = ob(buf) + x * TB;
       if (wave_live && (!CAUSAL || 32 * t + 31 >= kw0)) {
         f32x16 s = {}, dp = {};
         v8 kk[KS];
@@ -2723,8 +2746,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, FA_BWD_KV_OCC) void attn_bwd_dkdv_d
         v8 pf[2], dsf[2];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 l4 = *(const f32x4*)(&ls[buf][32 * x + 8 * q4 + 4 * hi]);
-          const f32x4 d4 = *(const f32x4*)(&dls[buf][32 * x + 8 * q4 + 4 * hi]);
+          const f32x4 l4 = *(const f32x4*)(ls(buf) + 32 * x + 8 * q4 + 4 * hi);
+          const f32x4 d4 = *(const f32x4*)(dls(buf) + 32 * x + 8 * q4 + 4 * hi);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * q4 + e;
