@@ -1563,6 +1563,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
   // (the staging array's smaller alignment places it after the tiles, whose
   // addresses then fit the LDS instructions' 16-bit offsets)
   __shared__ __attribute__((aligned(16))) unsigned char ostage[NW * 32 * D * 2];
+  // The kernel holds more values than its 256 registers, and scratch reloads
+  // in the loop would wait on the vector-memory counter, that is on the tile
+  // copies in flight. So each wave keeps its lanes' operand-read offsets
+  // (koff, voff) and its Q operand in LDS and reads them back where used,
+  // indexed by a lane index the compiler cannot hoist (fresh_lane), so that
+  // nothing derived from them stays live across the loop. Q is read as
+  // 16-byte pieces: a 32-byte LDS load is split without the information that
+  // tells its address apart from the copies' destinations, and then waits
+  // for every copy.
+  __shared__ int ores[NW][2 * KS + DB][64];
+  __shared__ i32x4 qres[NW][2 * KS][64];
   auto kbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? k0s : k1s; };
   auto vbuf = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? v0s : v1s; };
 
@@ -1595,6 +1606,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
 #pragma unroll
     for (int x = 0; x < 2; ++x)
       koff[2 * st + x] = (ln & 31) * D + (((4 * st + 2 * (ln >> 5) + x) ^ k8_swz<D>(ln & 31)) << 4);
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i) ores[wave][i][lane] = koff[i];
   // V^T operand of P V block db, read q at voff[db] + 8 * q * D: key row
   // 32*(group/2) + 8q + (i/2), head dims 32db + 16*(group%2) + 8*(i%2) + [0, 8).
   int voff[DB];
@@ -1604,6 +1617,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
       voff[db] = r * D + (((2 * db + (g & 1)) ^ v8_swz<D>(r)) << 4) + 8 * (i & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) ores[wave][2 * KS + db][lane] = voff[db];
   }
   const RowRange rr = row_range_at<BR, BC, CAUSAL>(p, bh, qt, wave, l32);
   const size_t kv_head = (size_t)rr.kv_bh * N * D;  // bytes
@@ -1614,6 +1629,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
     for (int s = 0; s < KS; ++s) {
       const int off = row * D + 64 * s + 32 * hi;
       qf[s] = __builtin_shufflevector(load16(rq, off), load16(rq, off + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qres[wave][2 * s][lane] = __builtin_shufflevector(qf[s], qf[s], 0, 1, 2, 3);
+      qres[wave][2 * s + 1][lane] = __builtin_shufflevector(qf[s], qf[s], 4, 5, 6, 7);
     }
   }
   const auto rsK = buffer_rsrc((const unsigned char*)p.k + kv_head, rr.kl * D);
@@ -1640,14 +1660,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
     for (int t = 0; t < KS + LA; ++t) {
       if (t < KS) {
         const unsigned char* b = kb + 32 * h * D;
-        ring[t % (LA + 1)] = __builtin_shufflevector(*(const i32x4*)(b + koff[2 * t]),
-                                                     *(const i32x4*)(b + koff[2 * t + 1]),
+        const int k0 = ores[wave][2 * t][fresh_lane()], k1 = ores[wave][2 * t + 1][fresh_lane()];
+        ring[t % (LA + 1)] = __builtin_shufflevector(*(const i32x4*)(b + k0), *(const i32x4*)(b + k1),
                                                      0, 1, 2, 3, 4, 5, 6, 7);
       }
       const int v = t - LA;
-      if (v >= 0)  // formats 0/0: fp8 e4m3 operands; E8M0 scales 127 = 1.0
-        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[v % (LA + 1)], qf[v], s, 0, 0, 0,
-                                                            127, 0, 127);
+      if (v >= 0) {  // formats 0/0: fp8 e4m3 operands; E8M0 scales 127 = 1.0
+        const i32x8 q = __builtin_shufflevector(qres[wave][2 * v][fresh_lane()],
+                                                qres[wave][2 * v + 1][fresh_lane()], 0, 1, 2, 3, 4, 5, 6, 7);
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[v % (LA + 1)], q, s, 0, 0, 0, 127, 0, 127);
+      }
     }
   };
 
@@ -1767,7 +1789,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
 #pragma unroll
     for (int t = 0; t < DB + LA; ++t) {
       if (t < DB) {
-        const unsigned char* a = vb + voff[t];
+        const unsigned char* a = vb + ores[wave][2 * KS + t][fresh_lane()];
         i32x8 v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
