@@ -1653,21 +1653,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
     }
   };
   // S^T = K Q^T over keys [32h, 32h + 32) of the K tile at kb
-  auto scores = [&](const unsigned char* kb, int h, f32x16& s) __attribute__((always_inline)) {
+  auto scores = [&](const unsigned char* kb, int h, f32x16& s, int fl) __attribute__((always_inline)) {
     s = f32x16{};
     i32x8 ring[LA + 1];
 #pragma unroll
     for (int t = 0; t < KS + LA; ++t) {
       if (t < KS) {
         const unsigned char* b = kb + 32 * h * D;
-        const int k0 = ores[wave][2 * t][fresh_lane()], k1 = ores[wave][2 * t + 1][fresh_lane()];
+        const int k0 = ores[wave][2 * t][fl], k1 = ores[wave][2 * t + 1][fl];
         ring[t % (LA + 1)] = __builtin_shufflevector(*(const i32x4*)(b + k0), *(const i32x4*)(b + k1),
                                                      0, 1, 2, 3, 4, 5, 6, 7);
       }
       const int v = t - LA;
       if (v >= 0) {  // formats 0/0: fp8 e4m3 operands; E8M0 scales 127 = 1.0
-        const i32x8 q = __builtin_shufflevector(qres[wave][2 * v][fresh_lane()],
-                                                qres[wave][2 * v + 1][fresh_lane()], 0, 1, 2, 3, 4, 5, 6, 7);
+        const i32x8 q = __builtin_shufflevector(qres[wave][2 * v][fl], qres[wave][2 * v + 1][fl], 0, 1, 2, 3,
+                                                4, 5, 6, 7);
         s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ring[v % (LA + 1)], q, s, 0, 0, 0, 127, 0, 127);
       }
     }
@@ -1773,7 +1773,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
     lx += rx;
   };
   // O^T += V^T P^T over the tile in vb: p0, p1 the rounded P' of its halves.
-  auto pv = [&](const unsigned char* vb, const i32x4& p0, const i32x4& p1)
+  auto pv = [&](const unsigned char* vb, const i32x4& p0, const i32x4& p1, int fl)
       __attribute__((always_inline)) {
     i32x8 b;
 #pragma unroll
@@ -1789,7 +1789,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
 #pragma unroll
     for (int t = 0; t < DB + LA; ++t) {
       if (t < DB) {
-        const unsigned char* a = vb + ores[wave][2 * KS + t][fresh_lane()];
+        const unsigned char* a = vb + ores[wave][2 * KS + t][fl];
         i32x8 v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1814,12 +1814,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
                        f32x16& x, f32x16& y, auto has_next, auto mask_a, auto mask_b)
       __attribute__((always_inline)) {
     constexpr bool HN = decltype(has_next)::value;
+    const int fl = fresh_lane();  // this iteration's lane index (not held across iterations)
     if constexpr (HN) {
-      scores(kb, 0, x);
-      scores(kb, 1, y);
+      scores(kb, 0, x, fl);
+      scores(kb, 1, y, fl);
     }
     probs(s1, p1, BC * t + 32, mask_a, std::true_type{}, p0);
-    pv(vb, p0, p1);
+    pv(vb, p0, p1, fl);
     if constexpr (HN) probs(x, p0, BC * (t + 1), mask_b, std::false_type{}, p1);
   };
   auto copies = [&](int t, unsigned char* kx, unsigned char* vx) __attribute__((always_inline)) {
@@ -1837,8 +1838,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
   wait_vmem();
   __syncthreads();
   if (rr.wnt > 0) {
-    scores(k0s, 0, sB);
-    scores(k0s, 1, sA);
+    const int fl = fresh_lane();
+    scores(k0s, 0, sB, fl);
+    scores(k0s, 1, sA, fl);
     if (0 < rr.wfull) probs(sB, p0, 0, std::false_type{}, std::false_type{}, p1);
     else probs(sB, p0, 0, std::true_type{}, std::false_type{}, p1);
   }
