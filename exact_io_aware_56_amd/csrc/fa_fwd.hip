@@ -1463,20 +1463,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe(Params p) {
   }
   // The rest: the last steady iterations, the wave's last tiles (the masked
   // one among them), then the iterations in which only other waves of the
-  // workgroup still compute. Masks are applied wherever a half may need one
-  // (an unneeded mask changes nothing); three variants keep the code small.
-  for (; t < rr.nt; ++t) {
-    const int q = t & 1;
-    unsigned char* kb = kbuf(q ^ 1);
-    unsigned char* vb = vbuf(q);
-    unsigned char* vx = vbuf(q ^ 1);
-    copies(t, kbuf(q), vx);
-    if (t < rr.wnt) {
-      if (t + 1 < rr.wfull) iteration(t, kb, vb, std::true_type{}, std::false_type{}, std::false_type{});
-      else if (t + 1 < rr.wnt) iteration(t, kb, vb, std::true_type{}, std::true_type{}, std::true_type{});
-      else iteration(t, kb, vb, std::false_type{}, std::true_type{}, std::false_type{});
-    }
-    sync_after(vx);
+  // workgroup still compute. One variant with every mask applied (an
+  // unneeded mask changes nothing) and the next tile always scored: past the
+  // wave's last tile that tile's keys are all masked for its rows (causal
+  // bound or key_len; the buffer holds finite stale or zero data), so it adds
+  // nothing. t is even here, so the pass is unrolled over the two buffer
+  // parities as above: with a buffer chosen at run time the compiler cannot
+  // tell the operand reads from the copies in flight and waits for every copy.
+  for (; t < rr.nt; t += 2) {
+    static_for<2>([&](auto P) __attribute__((always_inline)) {
+      constexpr int q = decltype(P)::value;
+      const int tt = t + q;
+      if (tt < rr.nt) {  // workgroup-uniform: every wave reaches the barrier
+        copies(tt, kbuf(q), vbuf(q ^ 1));
+        if (tt < rr.wnt)
+          iteration(tt, kbuf(q ^ 1), vbuf(q), std::true_type{}, std::true_type{}, std::true_type{});
+        sync_after(vbuf(q ^ 1));
+      }
+    });
   }
   // Every copy has landed and every wave is done with K and V: the buffers
   // now stage O (8 KB per wave for D = 128, two waves per buffer).
