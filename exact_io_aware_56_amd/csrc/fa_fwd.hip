@@ -1850,8 +1850,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
   }
   __syncthreads();  // K of tile 0 is read by every wave before its buffer is refilled
   // Iterations [0, ts): unmasked with a next tile, two per pass (the K/V
-  // buffers alternate, and so do the roles of sA and sC); then the rest one
-  // at a time with sA as s1, sC moved into sA after each.
+  // buffers alternate, and so do the roles of sA and sC).
   const int ts = max(0, rr.wfull - 1);
   int t = 0;
   for (; t + 2 <= ts; t += 2) {
@@ -1862,19 +1861,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
     iteration(t + 1, k0s, v1s, sC, sB, sA, std::true_type{}, std::false_type{}, std::false_type{});
     sync_after();
   }
-  for (; t < rr.nt; ++t) {
-    const int q = t & 1;
-    copies(t, kbuf(q), vbuf(q ^ 1));
-    if (t < rr.wnt) {
-      if (t + 1 < rr.wfull)
-        iteration(t, kbuf(q ^ 1), vbuf(q), sA, sB, sC, std::true_type{}, std::false_type{}, std::false_type{});
-      else if (t + 1 < rr.wnt)
-        iteration(t, kbuf(q ^ 1), vbuf(q), sA, sB, sC, std::true_type{}, std::true_type{}, std::true_type{});
-      else
-        iteration(t, kbuf(q ^ 1), vbuf(q), sA, sB, sC, std::false_type{}, std::true_type{}, std::false_type{});
-      sA = sC;
+  // The rest as in attn_fwd_pipe: one variant with every mask applied and
+  // the next tile always scored (past the wave's last tile its keys are all
+  // masked), unrolled over the two buffer parities (t is even here) with the
+  // score buffers rotating as in the pass above.
+  for (; t < rr.nt; t += 2) {
+    if (t < rr.nt) {  // workgroup-uniform
+      copies(t, k0s, v1s);
+      if (t < rr.wnt)
+        iteration(t, k1s, v0s, sA, sB, sC, std::true_type{}, std::true_type{}, std::true_type{});
+      sync_after();
     }
-    sync_after();
+    if (t + 1 < rr.nt) {
+      copies(t + 1, k1s, v0s);
+      if (t + 1 < rr.wnt)
+        iteration(t + 1, k0s, v1s, sC, sB, sA, std::true_type{}, std::true_type{}, std::true_type{});
+      sync_after();
+    }
   }
   // O / l through this wave's own staging slice (K/V buffers stay free);
   // LSE from the unrounded sum
