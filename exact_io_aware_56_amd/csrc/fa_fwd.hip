@@ -91,7 +91,8 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 #define FA_WIDE_WAVES 8  // waves per workgroup of the pipelined kernel
 #endif
 #ifndef FA_PIPE_LOOKAHEAD
-#define FA_PIPE_LOOKAHEAD 1  // pipelined kernel: LDS operand reads issued this many MFMAs ahead
+#define FA_PIPE_LOOKAHEAD 0  // pipelined kernels: LDS operand reads issued this many MFMAs ahead
+                             // (0: two for head dim 128 over whole V rows, else one)
 #endif
 #ifndef FA_PIPE_IGLP
 #define FA_PIPE_IGLP 3  // pipelined kernel: the compiler's MFMA/exp interleave for each half-step (-1: none)
@@ -1088,7 +1089,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe(Params p) {
   constexpr int NVC = TBV / 1024;  // 1 KB copies per 16-bit V tile
   constexpr int NDMAV = NVC / NW;  // V copies per wave per tile
   constexpr int NPV = 2 * DB;  // PV MFMA steps per half (2 x 16 keys)
-  constexpr int LA = FA_PIPE_LOOKAHEAD;
+  constexpr int LA = FA_PIPE_LOOKAHEAD > 0 ? FA_PIPE_LOOKAHEAD : (D == 128 && DV == D ? 2 : 1);
   static_assert(F8 || NKC % NW == 0, "16-bit tiles must split into 1 KB copies per wave");
   static_assert(F8 || NVC % NW == 0, "16-bit V tiles must split into 1 KB copies per wave");
 
@@ -1557,7 +1558,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
   constexpr int CPR = D / 16;   // 16-byte slots per row
   constexpr int NC = TB / 1024;  // 1 KB copies per tile
   constexpr int ND = (NC + NW - 1) / NW;  // copies per wave per tile (some idle)
-  constexpr int LA = FA_PIPE_LOOKAHEAD;
+  constexpr int LA = FA_PIPE_LOOKAHEAD > 0 ? FA_PIPE_LOOKAHEAD : 1;
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
 
   __shared__ __attribute__((aligned(1024))) unsigned char k0s[TB];
