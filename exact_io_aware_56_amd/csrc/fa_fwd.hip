@@ -1159,11 +1159,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe(Params p) {
   // One query tile of one head, start to finish.
   auto process = [&](int bh, int qt) __attribute__((always_inline)) {
   // Lane-derived values are recomputed per work item from a lane index the
-  // compiler cannot hoist, so that they are not kept live (and spilled) across
-  // the items: 16-bit d = 128 spills 24 instead of 48 bytes per lane and fetches
-  // 22.7 MB less per launch at the long causal workload. The fp8 and column-slice
-  // instances keep an opaque copy of the kernel's lane index (measured 0.5%
-  // faster there).
+  // compiler cannot hoist, so that they are not kept live across the items
+  // (16-bit d = 128; when the kernel still spilled, this halved its scratch).
+  // The fp8 and column-slice instances keep an opaque copy of the kernel's
+  // lane index (measured 0.5% faster there).
   constexpr bool FRESH = !F8 && DV == D;
   const int lx = FRESH ? fresh_lane() : lane;   // slots, rows, epilogue
   const int ln = FRESH ? lx : pinned_int(lane);  // operand read offsets
@@ -1568,9 +1567,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe8(Params p) {
   // (the staging array's smaller alignment places it after the tiles, whose
   // addresses then fit the LDS instructions' 16-bit offsets)
   __shared__ __attribute__((aligned(16))) unsigned char ostage[NW * 32 * D * 2];
-  // The kernel holds more values than its 256 registers, and scratch reloads
-  // in the loop would wait on the vector-memory counter, that is on the tile
-  // copies in flight. So each wave keeps its lanes' operand-read offsets
+  // The kernel is at the edge of its 256 registers: with these values in
+  // registers it spilled, and scratch reloads in the loop wait on the
+  // vector-memory counter, that is on the tile copies in flight. So each
+  // wave keeps its lanes' operand-read offsets
   // (koff, voff) and its Q operand in LDS and reads them back where used,
   // indexed by a lane index the compiler cannot hoist (fresh_lane), so that
   // nothing derived from them stays live across the loop. Q is read as
